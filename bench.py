@@ -1,0 +1,269 @@
+"""Benchmark: ring AllReduce of N=8 float32 rank buffers of 1.2 GB each on one
+MI355X, through the C ABI of libar.so.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+                    [--workload large_grad_fp32] [--collective ring_allreduce]
+                    [--impl fused|step] [--cpu-sample 33554432 | --no-cpu-baseline]
+
+One "step" is one collective call over the whole workload (every rank buffer
+already resident in HBM).  W untimed calls, then K timed calls bracketed by
+torch.cuda.synchronize(); each call is also bracketed by HIP events recorded
+on the stream the library launches on.  Rank 0 prints one JSON line.
+
+The collectives work in place, so step k+1 reduces step k's output: after an
+AllReduce every rank holds the sum, and each further call multiplies the
+magnitude by about N.  Normal(0, 1e-3) inputs stay finite for more than 35
+calls at N = 8 (8^35 * 1e-3 < 3.4e38), so W + K is capped there; the kernels
+have no value-dependent control flow.
+
+value: algorithm bandwidth, T * itemsize / (wall time per call), as GB/s
+(1 GB = 1e9 bytes).  roofline: the fused kernel's algorithmic HBM bytes per
+launch (2 * N * T * itemsize for AllReduce: every input read once, every
+output written once) over its average event-timed duration, against the
+8 TB/s HBM peak.  cpu_baseline: the CPU checker (a literal NumPy ring
+simulation, single-threaded) timed on a bounded sample of the same inputs.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ring AllReduce algbw GB/s and % of HBM peak, N=8 fp32 1.2 GB/rank"
+HBM_PEAK_GBPS = 8000.0
+DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
+MAX_CALLS = 35
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="large_grad_fp32")
+    p.add_argument("--collective", default="ring_allreduce",
+                   choices=["ring_allreduce", "reduce_scatter", "allgather", "broadcast",
+                            "tree_allreduce"])
+    p.add_argument("--impl", default="fused", choices=["fused", "step"])
+    p.add_argument("--cpu-sample", type=int, default=1 << 25,
+                   help="elements per rank of the CPU checker's sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="also run torch copies of this many MiB (PMC scaling reference)")
+    p.add_argument("--jsonl", default=None, help="append the JSON line to this file too")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "kernels.hpp"):
+        with open(os.path.join(ROOT, "tree_allreduce_algorithms_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(workload, collective, impl):
+    """HBM bytes per launch from a committed PMC summary, if it was taken on the
+    current kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{collective}_{impl}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(collective, n, t, isz):
+    """HBM bytes the fused implementation must move per call."""
+    return {
+        "ring_allreduce": 2 * n * t * isz,     # read N inputs, write N outputs
+        "tree_allreduce": 2 * n * t * isz,
+        "reduce_scatter": (n + 1) * t * isz,   # read N, write the owner's chunk
+        "allgather": n * t * isz,              # read each chunk once, write N-1 copies
+        "broadcast": n * t * isz,
+    }[collective]
+
+
+def cpu_baseline(sample, dtype, collective, n):
+    import oracle
+    fn = {
+        "ring_allreduce": lambda x: oracle.ring_allreduce(x, "sum", dtype),
+        "tree_allreduce": lambda x: oracle.tree_allreduce(x, "sum", dtype),
+        "reduce_scatter": lambda x: oracle.ring_reduce_scatter(x, "sum", dtype),
+        "allgather": lambda x: oracle.ring_allgather(x, dtype),
+        "broadcast": lambda x: oracle.broadcast(x, 0, dtype),
+    }[collective]
+    t0 = time.perf_counter()
+    fn(sample)
+    secs = time.perf_counter() - t0
+    ts = len(sample[0])
+    isz = sample[0].dtype.itemsize
+    return {
+        "value": ts * isz / secs / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{collective} of N={n} rank buffers of {ts} {dtype} elements (the first "
+                  f"{ts} elements of each rank's input), literal NumPy ring simulation, "
+                  f"one thread, {secs:.2f} s",
+        "seconds": secs,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): the N logical ranks are N buffers in one GPU's HBM; no figure "
+              f"across several GPUs is produced.", file=sys.stderr)
+        sys.exit(2)
+    if args.warmup + args.steps > MAX_CALLS:
+        print(f"--warmup + --steps must stay <= {MAX_CALLS} (values grow by N per call)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_allreduce_algorithms_amd as ar
+    from tree_allreduce_algorithms_amd import binding, workloads
+
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    ar.lib()
+    ar.set_impl(args.impl)
+
+    w = workloads.WORKLOADS[args.workload]
+    n, t, isz = w.nranks, w.count, w.itemsize
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload={w.name} N={n} T={t} dtype={w.dtype} collective={args.collective} "
+          f"impl={args.impl}", file=sys.stderr, flush=True)
+    bufs = [workloads.device_rank(w.dist, w.dtype, t, w.seed, r, dev, w.params) for r in range(n)]
+    torch.cuda.synchronize()
+
+    sample = None
+    if not args.no_cpu_baseline:
+        ts = min(args.cpu_sample, t)
+        if w.dtype == "bfloat16":
+            sample = [b[:ts].view(torch.int16).cpu().numpy().view(np.uint16) for b in bufs]
+        else:
+            sample = [b[:ts].cpu().numpy() for b in bufs]
+
+    call = {
+        "ring_allreduce": lambda: ar.ring_allreduce(bufs),
+        "tree_allreduce": lambda: ar.tree_allreduce(bufs),
+        "reduce_scatter": lambda: ar.reduce_scatter(bufs),
+        "allgather": lambda: ar.allgather(bufs),
+        "broadcast": lambda: ar.broadcast(bufs, root=0),
+    }[args.collective]
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    print(f"[bench] warmup done, timing {args.steps} calls", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    event_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    finite = bool(all(torch.isfinite(b[:1 << 20].float()).all().item() for b in bufs[:2]))
+
+    ms_per_step = wall / args.steps * 1e3
+    value = t * isz / (wall / args.steps) / 1e9
+    launch_ms = sum(event_ms) / len(event_ms)
+    alg = algorithmic_bytes(args.collective, n, t, isz)
+    achieved = alg / (launch_ms * 1e-3) / 1e9
+    launches = 1 if args.impl == "fused" else ar.expected_steps(args.collective, n)
+    traffic = traffic_from_profile(w.name, args.collective, args.impl)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_TAG[w.dtype],
+        "device": torch.cuda.get_device_name(dev),
+        "data": "synthetic",
+        "config": {"workload": w.name, "collective": args.collective, "impl": args.impl,
+                   "nranks": n, "count_per_rank": t, "rank_bytes": t * isz,
+                   "distribution": w.dist, "params": w.params, "seed": w.seed},
+        "pct_of_hbm_peak": round(100.0 * alg / (wall / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg if launches == 1 else None,
+            "algorithmic_bytes_per_call": alg,
+            "launches_per_step": launches,
+            "event_ms_mean": round(launch_ms, 4),
+            "event_ms_min": round(min(event_ms), 4),
+            "event_ms_max": round(max(event_ms), 4),
+        },
+        "outputs_finite": finite,
+    }
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ce0.record(stream)
+        reps = 5
+        for _ in range(reps):
+            dst.copy_(src)
+        ce1.record(stream)
+        torch.cuda.synchronize()
+        ms = ce0.elapsed_time(ce1) / reps
+        result["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes,
+                                      "ms": round(ms, 4),
+                                      "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+        del src, dst
+
+    del bufs
+    torch.cuda.empty_cache()
+    if sample is not None:
+        print(f"[bench] timing the CPU checker on {len(sample[0])} elements per rank",
+              file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(sample, w.dtype, args.collective, n)
+
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.jsonl:
+        with open(args.jsonl, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

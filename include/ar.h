@@ -1,0 +1,191 @@
+/*
+ * ar.h -- ring / tree collectives over N rank buffers held in ONE GPU's HBM.
+ *
+ * C ABI of libar.so (HIP kernels for gfx950 / MI355X).  N logical ranks are N
+ * separate device buffers of `count` elements each; a "send" from rank r to
+ * rank d is a read of r's buffer and a write (or read-modify-write) of d's.
+ *
+ * Sources, cited by page title and section:
+ *   [L09] "第09讲：网络通信基础与集合通信 Collective 原语直觉" (Lecture 09,
+ *         collective primitives): 3.1 Broadcast, 3.4 reduction operators,
+ *         3.5 AllReduce, 3.6 ReduceScatter, 3.7 AllGather, 3.9 AllReduce =
+ *         ReduceScatter + AllGather, 4.2-4.4 ring, 5.2 double binary tree.
+ *   [CH4] "4. 通信模式：集合通信（AllReduce、AllGather等）原理与实现"
+ *         (Chapter 4, communication patterns): 4.3.1 ring, 4.3.2 tree.
+ *   [SCR] "从零实现集合通信" (Collectives from scratch): section "two-pass
+ *         ring allreduce" (两趟实现 ring allreduce) and its cost table.
+ *
+ * Conventions shared by every collective below
+ * --------------------------------------------
+ * bufs    HOST array of `nranks` DEVICE pointers; bufs[r] is rank r's buffer
+ *         of `count` contiguous elements of `dtype`.  Every buffer must be
+ *         aligned to the element size, and no two buffers may overlap.  The
+ *         caller allocates and owns every buffer; the library never
+ *         allocates user memory and keeps no pointer after returning (the
+ *         pointers travel inside kernel arguments).
+ * nranks  N, 1 <= N <= AR_MAX_RANKS.
+ * count   T, elements per rank.  Chunk layout: C = ceil(T/N), chunk c =
+ *         [c*C, min(T, (c+1)*C)); only trailing chunks are short, and a chunk
+ *         is empty when c*C >= T.  Rank c owns chunk c.
+ * stream  a hipStream_t passed as void* (NULL = the null stream).  Calls are
+ *         asynchronous and stream-ordered: they enqueue kernels and return;
+ *         the library never synchronises.  Completion is observed through
+ *         the stream.  All buffers are updated IN PLACE.
+ * Arithmetic (the receiver stores `local (+) incoming`, as in the pages'
+ *         per-hop in-place add [L09 7.1][CH4 4.3.1]):
+ *           AR_INT32    two's-complement wrap-around for SUM and PROD;
+ *           AR_FLOAT32  one IEEE binary32 operation, round to nearest even,
+ *                       subnormals kept, never fused or reassociated;
+ *           AR_BFLOAT16 widen both to binary32, apply the op, round back to
+ *                       bfloat16 to nearest even after EVERY hop (NaN ->
+ *                       quiet NaN, sign and top payload kept);
+ *           MAX / MIN   keep the local value unless the incoming one compares
+ *                       strictly greater / smaller.
+ *         The ring calls reproduce the ring's order per element exactly
+ *         (chunk c folds ranks c+1, c+2, ..., c); the tree call reproduces the
+ *         binomial double tree's pairing.  Results are therefore bit-exact
+ *         and independent of the implementation chosen by ar_set_impl().
+ * Errors  reported synchronously BEFORE anything is enqueued, so a failing
+ *         call has no effect:
+ *           AR_ERROR_INVALID_ARGUMENT  bufs or an entry NULL; nranks out of
+ *               range; a pointer not aligned to the element size; two buffer
+ *               ranges overlapping; count * element size overflowing; root
+ *               out of range; unknown dtype or op;
+ *           AR_ERROR_UNSUPPORTED       a valid request this build lacks;
+ *           AR_ERROR_HIP               a kernel launch failed; the hipError_t
+ *               is kept for ar_last_hip_error().  (Faults during execution
+ *               surface at the caller's next synchronisation.)
+ *         count == 0 or nranks == 1 is a valid no-op (AR_SUCCESS, nothing
+ *         enqueued).
+ * Counters every successful call adds the logical inter-rank bytes of its
+ *         schedule (each transfer of k elements adds k * element size to the
+ *         sender's `sent` and the receiver's `recv`) and its schedule steps
+ *         to process-wide counters, whatever implementation runs.
+ */
+#ifndef AR_H
+#define AR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AR_MAX_RANKS 64
+#define AR_VERSION 1
+
+typedef enum {
+  AR_SUCCESS = 0,
+  AR_ERROR_INVALID_ARGUMENT = 1,
+  AR_ERROR_UNSUPPORTED = 2,
+  AR_ERROR_HIP = 3
+} ar_status_t;
+
+typedef enum { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BFLOAT16 = 2 } ar_dtype_t;
+
+/* The reduction operators listed in [L09 3.4]. */
+typedef enum { AR_SUM = 0, AR_PROD = 1, AR_MAX = 2, AR_MIN = 3 } ar_op_t;
+
+typedef enum {
+  AR_RING_ALLREDUCE = 0,
+  AR_REDUCE_SCATTER = 1,
+  AR_ALLGATHER = 2,
+  AR_BROADCAST = 3,
+  AR_TREE_ALLREDUCE = 4
+} ar_collective_t;
+
+/* How a collective is executed; results are bit-identical either way.
+ *   AR_IMPL_FUSED  one pass: every element's N inputs are read once, folded
+ *                  in the schedule's order in registers, and the result is
+ *                  written once per destination rank.
+ *   AR_IMPL_STEP   the schedule literally: one kernel launch per ring step or
+ *                  tree round, each applying all of that step's transfers. */
+typedef enum { AR_IMPL_FUSED = 0, AR_IMPL_STEP = 1 } ar_impl_t;
+
+/* Ring AllReduce [L09 3.5, 3.9, 4.3][CH4 4.3.1][SCR two-pass ring]:
+ * ReduceScatter then AllGather.  Afterwards every bufs[r] holds, at element
+ * i of chunk c, the fold x[c+1][i] (+) ... (+) x[c][i] taken in ring order
+ * (each hop: the receiving rank's own value (+) the incoming partial). */
+ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                              ar_op_t op, void* stream);
+
+/* Ring ReduceScatter [L09 3.6][SCR two-pass ring, first pass]: N-1 steps; at
+ * step t rank r forwards chunk (r-t-1) mod N to rank r+1, which stores
+ * own (+) incoming.  Afterwards chunk r of bufs[r] holds the full reduction of
+ * chunk r (same fold as ar_ring_allreduce).  The contents of the other chunks
+ * of every buffer are UNSPECIFIED afterwards (partials or inputs, depending
+ * on the implementation). */
+ar_status_t ar_reduce_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                              ar_op_t op, void* stream);
+
+/* Ring AllGather [L09 3.7][SCR two-pass ring, second pass]: the input of
+ * rank r is chunk r of bufs[r] (its other chunks are ignored and
+ * overwritten); N-1 steps, at step t rank r forwards chunk (r-t) mod N to
+ * rank r+1, which overwrites.  Afterwards every buffer holds every rank's
+ * chunk. */
+ar_status_t ar_allgather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                         void* stream);
+
+/* Broadcast [L09 3.1][SCR cost table: T bytes over a log2 N tree]: every
+ * bufs[r] ends equal to bufs[root].  Schedule (and counters): a binomial tree
+ * on roles (r - root) mod N, ceil(log2 N) rounds. */
+ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
+                         void* stream);
+
+/* Double-binary-tree AllReduce [L09 5.2][CH4 4.3.2][SCR cost table:
+ * 2 log2 N steps].  Two binomial trees reduce toward role 0 and broadcast
+ * back, each over half the data: tree 0 handles elements [0, ceil(T/2)) with
+ * role == rank, tree 1 handles [ceil(T/2), T) with role == N-1-rank.  Reduce
+ * round k: role q (q mod 2^(k+1) == 0, q + 2^k < N) stores
+ * own (+) value of role q + 2^k.  Every bufs[r] ends with role 0's result. */
+ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                              ar_op_t op, void* stream);
+
+/* ---- host-only helpers: no GPU work, usable without a GPU ---------------- */
+
+/* C = ceil(count / nranks); 0 if nranks < 1. */
+size_t ar_chunk_size(int nranks, size_t count);
+
+/* Bounds [*begin, *end) of chunk `chunk`; AR_ERROR_INVALID_ARGUMENT if nranks
+ * or chunk is out of range or an output pointer is NULL. */
+ar_status_t ar_chunk_range(int nranks, size_t count, int chunk, size_t* begin, size_t* end);
+
+/* Logical bytes each rank sends and receives in one call of `coll` with these
+ * arguments ([SCR cost table]; e.g. 2T(N-1)/N per rank for the ring when N
+ * divides T).  sent and recv are caller arrays of nranks uint64_t.  `root`
+ * is used for AR_BROADCAST only. */
+ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype,
+                              int root, uint64_t* sent, uint64_t* recv);
+
+/* Schedule steps of one call: 2(N-1) ring AllReduce, N-1 ReduceScatter and
+ * AllGather, ceil(log2 N) Broadcast, 2 ceil(log2 N) tree AllReduce; -1 on a
+ * bad argument. */
+int ar_expected_steps(ar_collective_t coll, int nranks);
+
+/* Process-wide cumulative counters since load or the last reset.  Copies the
+ * first nranks entries (nranks <= AR_MAX_RANKS) into sent / recv, and the
+ * total schedule steps into *steps (any output may be NULL).  Thread-safe. */
+ar_status_t ar_counters_read(int nranks, uint64_t* sent, uint64_t* recv, uint64_t* steps);
+void ar_counters_reset(void);
+
+/* Process-wide choice of implementation for subsequent calls (initially
+ * AR_IMPL_FUSED, or AR_IMPL_STEP when the environment variable AR_IMPL is
+ * "step" at load).  Thread-safe. */
+ar_status_t ar_set_impl(ar_impl_t impl);
+ar_impl_t ar_get_impl(void);
+
+/* Static description of a status code. */
+const char* ar_status_string(ar_status_t status);
+
+/* hipError_t of this thread's most recent AR_ERROR_HIP (0 if none). */
+int ar_last_hip_error(void);
+
+/* AR_VERSION of the loaded library. */
+int ar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_H */

@@ -1,0 +1,403 @@
+"""GPU parity: the HIP collectives (through the C ABI) against the CPU oracle.
+
+Bar: bit-exact for every dtype.  The fused kernels fold each element in the
+ring's (or the tree's) own order, so float32 and bfloat16 results must equal
+the literal step-by-step simulation bit for bit, as must the step-by-step
+kernels.  NaN payloads are the one exception (x86 and the GPU produce
+different default NaNs); where NaN can arise, NaN positions are compared
+instead of NaN bits.
+
+Small and medium shapes compare every element of every rank.  Full-size
+workloads (1.2 GB per rank and up) compare sampled windows -- chunk and tree
+boundaries, the ends, seeded random positions -- which the oracle simulates
+on the global chunk layout, and check properties that hold at any size on
+the device (every rank identical, AllGather after ReduceScatter equals
+AllReduce, Broadcast equals the root).
+"""
+
+import os
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_allreduce_algorithms_amd as ar
+from tree_allreduce_algorithms_amd import binding, workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+IMPLS = ("fused", "step")
+TORCH_DT = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}
+
+
+def announce(msg):
+    print(f"[gpu-parity] {msg}", file=sys.__stderr__, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert os.path.exists(binding.LIB_PATH), "libar.so is not built"
+    ar.lib()
+    yield
+    ar.set_impl("fused")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def to_dev(arrs, dtype):
+    if dtype == "bfloat16":
+        return [torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(DEV) for a in arrs]
+    return [torch.from_numpy(np.ascontiguousarray(a).copy()).to(DEV) for a in arrs]
+
+
+def to_host(t, dtype):
+    if dtype == "bfloat16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def same_bits(got, want, dtype):
+    """Bitwise equality; NaN compared by position for the float types."""
+    if dtype == "int32" or got.size == 0:
+        return np.array_equal(got, want)
+    f = oracle.bf16_to_f32 if dtype == "bfloat16" else (lambda a: a)
+    gn, wn = np.isnan(f(got)), np.isnan(f(want))
+    return np.array_equal(gn, wn) and np.array_equal(got[~gn], want[~wn])
+
+
+def assert_same(got, want, dtype, what):
+    if not same_bits(got, want, dtype):
+        bad = np.flatnonzero(got != want)
+        raise AssertionError(f"{what}: {bad.size} elements differ, first at {bad[:5]}: "
+                             f"got {got[bad[:5]]} want {want[bad[:5]]}")
+
+
+CALLS = {
+    "ring_allreduce": (lambda b, op, root: ar.ring_allreduce(b, op=op),
+                       lambda x, op, dt, root, **k: oracle.ring_allreduce(x, op, dt, **k)),
+    "reduce_scatter": (lambda b, op, root: ar.reduce_scatter(b, op=op),
+                       lambda x, op, dt, root, **k: oracle.ring_reduce_scatter(x, op, dt, **k)),
+    "allgather": (lambda b, op, root: ar.allgather(b),
+                  lambda x, op, dt, root, **k: oracle.ring_allgather(x, dt, **k)),
+    "broadcast": (lambda b, op, root: ar.broadcast(b, root=root),
+                  lambda x, op, dt, root, **k: oracle.broadcast(x, root, dt, **k)),
+    "tree_allreduce": (lambda b, op, root: ar.tree_allreduce(b, op=op),
+                       lambda x, op, dt, root, **k: oracle.tree_allreduce(x, op, dt, **k)),
+}
+
+
+def compare_collective(coll, x, dtype, op, root, impls=IMPLS, check_counters=True):
+    """Run `coll` on device copies of x with each implementation; compare every
+    element the collective defines (owned chunks only for ReduceScatter)."""
+    n, t = len(x), len(x[0])
+    want = CALLS[coll][1](x, op, dtype, root).bufs
+    owned = oracle.chunk_layout(n, t)
+    for impl in impls:
+        announce(f"{coll} impl={impl} n={n} t={t} dtype={dtype} op={op} root={root}")
+        ar.set_impl(impl)
+        bufs = to_dev(x, dtype)
+        ar.reset_counters()
+        CALLS[coll][0](bufs, op, root)
+        torch.cuda.synchronize()
+        for r in range(n):
+            got = to_host(bufs[r], dtype)
+            if coll == "reduce_scatter":
+                lo, hi = owned[r]
+                assert_same(got[lo:hi], want[r][lo:hi], dtype, f"{coll}/{impl} rank {r} owned chunk")
+            else:
+                assert_same(got, want[r], dtype, f"{coll}/{impl} rank {r}")
+        if check_counters:
+            sent, recv, steps = ar.counters(n)
+            esent, erecv = ar.expected_bytes(coll, n, t, dtype, root=root)
+            assert (sent, recv) == (esent, erecv)
+            assert steps == ar.expected_steps(coll, n)
+        del bufs
+    ar.set_impl("fused")
+
+
+# --- element-by-element cases -------------------------------------------------
+
+CASES = [
+    # name, N, T, dtype, dist, ops
+    ("small_int32", 4, 1024, "int32", "int_uniform", ("sum", "prod", "max", "min")),
+    ("ragged_fp32", 8, 100_003, "float32", "uniform_pm1", ("sum", "prod", "max", "min")),
+    ("ragged_bf16", 8, 100_003, "bfloat16", "uniform_pm1", ("sum", "prod", "max", "min")),
+    ("n64_fp32", 64, 70_001, "float32", "normal", ("sum",)),
+    ("n64_bf16", 64, 20_011, "bfloat16", "normal", ("sum", "max")),
+    ("n64_int32", 64, 9_001, "int32", "int_uniform", ("sum", "min")),
+    ("n5_tiny", 5, 23, "float32", "normal", ("sum", "min")),
+    ("t_below_n", 8, 3, "float32", "normal", ("sum",)),
+    ("t_one", 3, 1, "int32", "int_uniform", ("sum",)),
+    ("n2_bf16", 2, 4_099, "bfloat16", "normal", ("sum",)),
+    ("n3_int32", 3, 50_001, "int32", "int_uniform", ("sum", "prod")),
+    ("n7_fp32", 7, 30_000, "float32", "normal", ("sum",)),
+    ("n16_exact_tiles", 16, 16 * 2048, "float32", "normal", ("sum",)),
+    ("sweep_256", 4, 256, "float32", "uniform_pm1", ("sum",)),
+    ("sweep_262144", 4, 262_144, "float32", "uniform_pm1", ("sum",)),
+]
+
+
+def _params(dist, n):
+    if dist == "int_uniform":
+        return {"lo": -100, "hi": 100}
+    if dist == "normal":
+        return {"std": 1e-3}
+    return {}
+
+
+@pytest.mark.parametrize("coll", sorted(CALLS))
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_parity_elementwise(case, coll):
+    name, n, t, dtype, dist, ops = case
+    x = workloads.host_inputs(n, t, dtype, dist, seed=zlib.crc32(name.encode()) % 100_000, params=_params(dist, n))
+    root = (n - 1) // 2 if n > 1 else 0
+    for op in (ops if coll not in ("allgather", "broadcast") else ("sum",)):
+        compare_collective(coll, x, dtype, op, root)
+
+
+def test_parity_sweep_16mb():
+    w = workloads.WORKLOADS["sweep_4194304"]
+    x = workloads.workload_host_inputs(w)
+    for coll in ("ring_allreduce", "tree_allreduce"):
+        compare_collective(coll, x, w.dtype, "sum", 0)
+
+
+def test_parity_ddp_bucket_full():
+    w = workloads.WORKLOADS["ddp_bucket"]
+    x = workloads.workload_host_inputs(w)
+    compare_collective("ring_allreduce", x, w.dtype, "sum", 0)
+    compare_collective("tree_allreduce", x, w.dtype, "sum", 0, impls=("fused",))
+
+
+# --- edge cases -----------------------------------------------------------------
+
+def test_subnormals_are_kept():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(1, 1 << 23, size=(8, 4099), dtype=np.uint32)
+    sign = (rng.integers(0, 2, size=(8, 4099), dtype=np.uint32) << np.uint32(31))
+    x = [(bits[r] | sign[r]).view(np.float32) for r in range(8)]
+    for coll in ("ring_allreduce", "tree_allreduce"):
+        compare_collective(coll, x, "float32", "sum", 0)
+
+
+def test_signed_zero_nan_and_infinity_rules():
+    vals = np.array([0.0, -0.0, np.nan, np.inf, -np.inf, 1.0, -1.0, 3.0e38], dtype=np.float32)
+    rng = np.random.default_rng(9)
+    x = [vals[rng.integers(0, vals.size, size=5003)] for _ in range(5)]
+    for op in ("max", "min", "sum", "prod"):
+        for coll in ("ring_allreduce", "tree_allreduce"):
+            compare_collective(coll, x, "float32", op, 0)
+    xb = [oracle.f32_to_bf16_rne(a) for a in x]
+    for op in ("max", "min", "sum"):
+        compare_collective("ring_allreduce", xb, "bfloat16", op, 0)
+
+
+def test_int32_wraparound():
+    x = [np.full(1031, 2**31 - 1 - r, dtype=np.int32) for r in range(6)]
+    for op in ("sum", "prod"):
+        for coll in ("ring_allreduce", "tree_allreduce", "reduce_scatter"):
+            compare_collective(coll, x, "int32", op, 0)
+
+
+def test_allgather_ignores_non_owned_slots():
+    n, t = 8, 10_001
+    x = workloads.host_inputs(n, t, "float32", "normal", 21, {"std": 1.0})
+    for r, (lo, hi) in enumerate(oracle.chunk_layout(n, t)):
+        poisoned = np.full(t, np.nan, dtype=np.float32)
+        poisoned[lo:hi] = x[r][lo:hi]
+        x[r] = poisoned
+    compare_collective("allgather", x, "float32", "sum", 0)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+def test_allgather_after_reduce_scatter_equals_allreduce(dtype):
+    n, t = 8, 200_003
+    dist = "int_uniform" if dtype == "int32" else "normal"
+    x = workloads.host_inputs(n, t, dtype, dist, 31, _params(dist, n))
+    results = {}
+    for impl in IMPLS:
+        ar.set_impl(impl)
+        a = to_dev(x, dtype)
+        ar.ring_allreduce(a)
+        b = to_dev(x, dtype)
+        ar.reduce_scatter(b)
+        ar.allgather(b)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert torch.equal(a[r].view(torch.int16 if dtype == "bfloat16" else a[r].dtype),
+                               b[r].view(torch.int16 if dtype == "bfloat16" else b[r].dtype))
+            assert torch.equal(a[r], a[0])
+        results[impl] = to_host(a[0], dtype)
+    assert np.array_equal(results["fused"], results["step"])
+    ar.set_impl("fused")
+
+
+def test_non_default_stream():
+    n, t = 4, 65_537
+    x = workloads.host_inputs(n, t, "float32", "normal", 41, {"std": 1.0})
+    want = oracle.ring_allreduce(x, "sum", "float32").bufs
+    s = torch.cuda.Stream()
+    bufs = to_dev(x, "float32")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ar.ring_allreduce(bufs)
+        ar.tree_allreduce(to_dev(x, "float32"))
+    s.synchronize()
+    for r in range(n):
+        assert_same(to_host(bufs[r], "float32"), want[r], "float32", f"rank {r}")
+
+
+def test_unaligned_buffers_are_rejected_untouched():
+    base = torch.arange(4 * 1001 + 4, dtype=torch.float32, device=DEV)
+    views = [base[1 + r * 1001: 1 + (r + 1) * 1001] for r in range(4)]   # 4-byte, not 16-byte
+    keep = base.clone()
+    status = binding.raw_call("ring_allreduce", [v.data_ptr() for v in views], 1001, "float32",
+                              op="sum", stream=0)
+    torch.cuda.synchronize()
+    assert status == binding.UNSUPPORTED
+    assert torch.equal(base, keep)
+
+
+# --- full-size workloads: sampled windows --------------------------------------
+
+WIN = 2048
+
+
+def _windows(t, cuts, seed, count=6):
+    rng = np.random.default_rng(seed)
+    starts = {0, max(0, t - WIN)}
+    for c in cuts:
+        starts.add(min(max(0, c - WIN // 2), max(0, t - WIN)))
+    for _ in range(count):
+        starts.add(int(rng.integers(0, max(1, t - WIN))))
+    return sorted((a, min(t, a + WIN)) for a in starts)
+
+
+def _device_inputs(w, count=None, n=None):
+    n = w.nranks if n is None else n
+    count = w.count if count is None else count
+    return [workloads.device_rank(w.dist, w.dtype, count, w.seed, r, DEV, w.params)
+            for r in range(n)]
+
+
+def _window_host(bufs, a, b, dtype):
+    return [to_host(t[a:b], dtype) for t in bufs]
+
+
+def check_windows(coll, bufs_before, run, dtype, op="sum", root=0, cuts=(), seed=0, ranks=None):
+    """Copy windows of the inputs, run the collective, then compare each window
+    with the oracle's windowed run on the global layout."""
+    n, t = len(bufs_before), bufs_before[0].numel()
+    wins = _windows(t, cuts, seed)
+    saved = [(a, b, _window_host(bufs_before, a, b, dtype)) for a, b in wins]
+    announce(f"{coll} n={n} t={t} dtype={dtype} windows={len(wins)}")
+    run(bufs_before)
+    torch.cuda.synchronize()
+    owned = oracle.chunk_layout(n, t)
+    for a, b, xin in saved:
+        want = CALLS[coll][1](xin, op, dtype, root, window_start=a, total=t).bufs
+        for r in (range(n) if ranks is None else ranks):
+            got = to_host(bufs_before[r][a:b], dtype)
+            if coll == "reduce_scatter":
+                lo, hi = max(owned[r][0], a) - a, min(owned[r][1], b) - a
+                if lo < hi:
+                    assert_same(got[lo:hi], want[r][lo:hi], dtype, f"window {a} rank {r}")
+            else:
+                assert_same(got, want[r], dtype, f"{coll} window [{a},{b}) rank {r}")
+
+
+def _ranks_identical(bufs):
+    v = [b.view(torch.int16) if b.dtype == torch.bfloat16 else b for b in bufs]
+    return all(torch.equal(v[0], x) for x in v[1:])
+
+
+@pytest.mark.parametrize("wname", ["large_grad_fp32", "large_grad_bf16"])
+def test_large_gradient_ring_allreduce(wname):
+    """N=8 rank buffers of 300,000,000 elements, in the launch configuration the
+    bench times (fused ring AllReduce), plus the step-by-step path."""
+    w = workloads.WORKLOADS[wname]
+    size = -(-w.count // w.nranks)
+    cuts = [c * size for c in range(1, w.nranks)]
+    for impl in IMPLS:
+        ar.set_impl(impl)
+        bufs = _device_inputs(w)
+        check_windows("ring_allreduce", bufs, lambda b: ar.ring_allreduce(b), w.dtype,
+                      cuts=cuts, seed=w.seed, ranks=[0, 3, 7])
+        assert _ranks_identical(bufs)
+        del bufs
+        torch.cuda.empty_cache()
+    ar.set_impl("fused")
+    # AllGather after ReduceScatter equals AllReduce, on the whole buffers
+    a = _device_inputs(w)
+    ar.ring_allreduce(a)
+    b = _device_inputs(w)
+    ar.reduce_scatter(b)
+    ar.allgather(b)
+    torch.cuda.synchronize()
+    for r in range(w.nranks):
+        assert torch.equal(a[r].view(torch.int16) if w.dtype == "bfloat16" else a[r],
+                           b[r].view(torch.int16) if w.dtype == "bfloat16" else b[r])
+    del a, b
+    torch.cuda.empty_cache()
+
+
+def test_large_sweep_point_ring_and_tree():
+    w = workloads.WORKLOADS["sweep_67108864"]
+    size = -(-w.count // w.nranks)
+    for coll, run, cuts in (
+            ("ring_allreduce", lambda b: ar.ring_allreduce(b), [c * size for c in range(1, 4)]),
+            ("tree_allreduce", lambda b: ar.tree_allreduce(b), [-(-w.count // 2)])):
+        for impl in IMPLS:
+            ar.set_impl(impl)
+            bufs = _device_inputs(w)
+            check_windows(coll, bufs, run, w.dtype, cuts=cuts, seed=7)
+            assert _ranks_identical(bufs)
+            del bufs
+    ar.set_impl("fused")
+    torch.cuda.empty_cache()
+
+
+def test_zero_n64_reduce_scatter_then_allgather_and_broadcast():
+    """N=64, T=16,777,217 float32: ReduceScatter then AllGather compared with the
+    oracle's AllReduce; Broadcast from rank 0 on fresh inputs."""
+    w = workloads.WORKLOADS["zero_n64"]
+    size = -(-w.count // w.nranks)
+    cuts = [c * size for c in range(1, w.nranks, 9)] + [63 * size]
+
+    def rs_then_ag(b):
+        ar.reduce_scatter(b)
+        ar.allgather(b)
+
+    for impl in IMPLS:
+        ar.set_impl(impl)
+        bufs = _device_inputs(w)
+        check_windows("ring_allreduce", bufs, rs_then_ag, w.dtype, cuts=cuts, seed=5,
+                      ranks=[0, 1, 31, 62, 63])
+        assert _ranks_identical(bufs)
+        del bufs
+        bufs = _device_inputs(w)
+        root_copy = bufs[0].clone()
+        announce(f"broadcast impl={impl} n=64 t={w.count}")
+        ar.broadcast(bufs, root=0)
+        torch.cuda.synchronize()
+        assert all(torch.equal(b, root_copy) for b in bufs)
+        del bufs, root_copy
+        torch.cuda.empty_cache()
+    ar.set_impl("fused")
+
+
+def test_rank_buffers_beyond_4_gib():
+    """Two ranks of 2^30 + 3 float32 each (just over 4 GiB per buffer): byte
+    offsets above 2^32 inside one buffer, with a ragged tail."""
+    t = (1 << 30) + 3
+    bufs = [workloads.device_rank("uniform_pm1", "float32", t, 17, r, DEV) for r in range(2)]
+    check_windows("ring_allreduce", bufs, lambda b: ar.ring_allreduce(b), "float32",
+                  cuts=[-(-t // 2)], seed=17)
+    assert _ranks_identical(bufs)
+    del bufs
+    torch.cuda.empty_cache()

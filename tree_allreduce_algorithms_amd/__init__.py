@@ -1,6 +1,26 @@
 """MI355X-native ring / tree collectives over N rank buffers on one GPU.
 
-The collectives live in a C-ABI shared library (``libar.so``, HIP kernels for
-gfx950) and this package is a thin ctypes binding with the same names.  The
-library is loaded on first use; if it has not been built the call raises.
+The collectives live in a C-ABI shared library (``libar.so``: HIP kernels for
+gfx950 plus the C ABI declared in ``include/ar.h``); this package is a thin
+ctypes binding with the same names.  The library is loaded on first use; if
+it has not been built the call raises.
 """
+
+from .binding import (  # noqa: F401
+    ArError,
+    allgather,
+    broadcast,
+    chunk_range,
+    chunk_size,
+    counters,
+    expected_bytes,
+    expected_steps,
+    get_impl,
+    lib,
+    raw_call,
+    reduce_scatter,
+    reset_counters,
+    ring_allreduce,
+    set_impl,
+    tree_allreduce,
+)

@@ -1,0 +1,219 @@
+"""ctypes binding of libar.so: the same calls as include/ar.h, plus torch glue.
+
+Argument marshalling only -- every collective runs in the library's HIP
+kernels.  The library is loaded on first use from this package's directory;
+if it is missing the call raises instead of falling back to anything else.
+"""
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libar.so")
+
+MAX_RANKS = 64
+
+SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR = 0, 1, 2, 3
+DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
+OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
+COLLECTIVES = {"ring_allreduce": 0, "reduce_scatter": 1, "allgather": 2, "broadcast": 3,
+               "tree_allreduce": 4}
+IMPLS = {"fused": 0, "step": 1}
+
+# name -> (restype, argtypes), in the order include/ar.h declares them
+_VP, _I, _SZ, _U64P = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint64)
+_PP = ctypes.POINTER(ctypes.c_void_p)
+SIGNATURES = {
+    "ar_ring_allreduce": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_reduce_scatter": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_allgather": (_I, [_PP, _I, _SZ, _I, _VP]),
+    "ar_broadcast": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_tree_allreduce": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_chunk_size": (_SZ, [_I, _SZ]),
+    "ar_chunk_range": (_I, [_I, _SZ, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
+    "ar_expected_bytes": (_I, [_I, _I, _SZ, _I, _I, _U64P, _U64P]),
+    "ar_expected_steps": (_I, [_I, _I]),
+    "ar_counters_read": (_I, [_I, _U64P, _U64P, _U64P]),
+    "ar_counters_reset": (None, []),
+    "ar_set_impl": (_I, [_I]),
+    "ar_get_impl": (_I, []),
+    "ar_status_string": (ctypes.c_char_p, [_I]),
+    "ar_last_hip_error": (_I, []),
+    "ar_version": (_I, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class ArError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        detail = ""
+        if status == HIP_ERROR:
+            detail = f" (hipError_t {lib().ar_last_hip_error()})"
+        msg = lib().ar_status_string(status).decode()
+        super().__init__(f"{where}: {msg}{detail}")
+
+
+def lib():
+    """The loaded libar.so (loads it on first call; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is not built; run "
+                        "`python -m tree_allreduce_algorithms_amd.build_lib` first")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def _check(status, where):
+    if status != SUCCESS:
+        raise ArError(status, where)
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[ctypes.c_void_p(int(p)) for p in ptrs])
+    return ctypes.cast(arr, _PP), arr
+
+
+# --- raw pointer calls (device addresses as ints) ----------------------------
+
+def raw_call(name, ptrs, count, dtype, op=None, root=None, stream=0):
+    """Call one collective on device pointers; returns the status code."""
+    pp, keep = _ptr_array(ptrs)
+    n = len(ptrs)
+    fn = getattr(lib(), "ar_" + name)
+    dt = DTYPES[dtype]
+    if name in ("ring_allreduce", "reduce_scatter", "tree_allreduce"):
+        status = fn(pp, n, count, dt, OPS[op], stream)
+    elif name == "allgather":
+        status = fn(pp, n, count, dt, stream)
+    elif name == "broadcast":
+        status = fn(pp, n, count, dt, root, stream)
+    else:
+        raise ValueError(name)
+    del keep
+    return status
+
+
+# --- torch glue ---------------------------------------------------------------
+
+def _torch_dtype_name(t):
+    import torch
+    names = {torch.int32: "int32", torch.float32: "float32", torch.bfloat16: "bfloat16"}
+    if t.dtype not in names:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return names[t.dtype]
+
+
+def _prep(tensors):
+    import torch
+    tensors = list(tensors)
+    if not tensors:
+        raise ValueError("need at least one rank tensor")
+    if len(tensors) > MAX_RANKS:
+        raise ValueError(f"at most {MAX_RANKS} ranks")
+    t0 = tensors[0]
+    for t in tensors:
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("rank buffers must be GPU tensors")
+        if t.device != t0.device or t.dtype != t0.dtype or t.numel() != t0.numel():
+            raise ValueError("rank buffers must share device, dtype and size")
+        if not t.is_contiguous():
+            raise ValueError("rank buffers must be contiguous")
+    return tensors, _torch_dtype_name(t0), t0.numel()
+
+
+def _stream_handle(tensors, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(tensors[0].device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _collective(name, tensors, op=None, root=None, stream=None):
+    tensors, dtype, count = _prep(tensors)
+    status = raw_call(name, [t.data_ptr() for t in tensors], count, dtype, op=op, root=root,
+                      stream=_stream_handle(tensors, stream))
+    _check(status, name)
+    return tensors
+
+
+def ring_allreduce(tensors, op="sum", stream=None):
+    """Ring AllReduce in place over the rank tensors (see ar_ring_allreduce)."""
+    return _collective("ring_allreduce", tensors, op=op, stream=stream)
+
+
+def reduce_scatter(tensors, op="sum", stream=None):
+    """Ring ReduceScatter in place: chunk r of tensors[r] ends fully reduced."""
+    return _collective("reduce_scatter", tensors, op=op, stream=stream)
+
+
+def allgather(tensors, stream=None):
+    """Ring AllGather in place: chunk r of tensors[r] is copied to every rank."""
+    return _collective("allgather", tensors, stream=stream)
+
+
+def broadcast(tensors, root=0, stream=None):
+    """Broadcast tensors[root] into every rank tensor."""
+    return _collective("broadcast", tensors, root=root, stream=stream)
+
+
+def tree_allreduce(tensors, op="sum", stream=None):
+    """Double-binary-tree AllReduce in place (see ar_tree_allreduce)."""
+    return _collective("tree_allreduce", tensors, op=op, stream=stream)
+
+
+# --- host-only helpers --------------------------------------------------------
+
+def chunk_size(nranks, count):
+    return lib().ar_chunk_size(nranks, count)
+
+
+def chunk_range(nranks, count, chunk):
+    lo, hi = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().ar_chunk_range(nranks, count, chunk, ctypes.byref(lo), ctypes.byref(hi)),
+           "chunk_range")
+    return lo.value, hi.value
+
+
+def expected_bytes(collective, nranks, count, dtype, root=0):
+    sent = (ctypes.c_uint64 * max(1, nranks))()
+    recv = (ctypes.c_uint64 * max(1, nranks))()
+    _check(lib().ar_expected_bytes(COLLECTIVES[collective], nranks, count, DTYPES[dtype], root,
+                                   sent, recv), "expected_bytes")
+    return list(sent)[:nranks], list(recv)[:nranks]
+
+
+def expected_steps(collective, nranks):
+    return lib().ar_expected_steps(COLLECTIVES[collective], nranks)
+
+
+def counters(nranks):
+    sent = (ctypes.c_uint64 * max(1, nranks))()
+    recv = (ctypes.c_uint64 * max(1, nranks))()
+    steps = ctypes.c_uint64()
+    _check(lib().ar_counters_read(nranks, sent, recv, ctypes.byref(steps)), "counters")
+    return list(sent)[:nranks], list(recv)[:nranks], steps.value
+
+
+def reset_counters():
+    lib().ar_counters_reset()
+
+
+def set_impl(impl):
+    _check(lib().ar_set_impl(IMPLS[impl]), "set_impl")
+
+
+def get_impl():
+    return {v: k for k, v in IMPLS.items()}[lib().ar_get_impl()]

@@ -1,0 +1,207 @@
+// C ABI of libar.so: argument validation, implementation dispatch, counters.
+//
+// Every call validates its arguments before touching the HIP runtime, so
+// argument errors are reported with nothing enqueued (and can be exercised
+// on a machine without a GPU).  Kernels run on the caller's stream; the
+// library never synchronises and never allocates.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "ar.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace {
+
+std::mutex g_counter_mu;
+uint64_t g_sent[AR_MAX_RANKS];
+uint64_t g_recv[AR_MAX_RANKS];
+uint64_t g_steps = 0;
+
+ar_impl_t impl_from_env() {
+  const char* v = std::getenv("AR_IMPL");
+  return (v != nullptr && std::strcmp(v, "step") == 0) ? AR_IMPL_STEP : AR_IMPL_FUSED;
+}
+std::atomic<int> g_impl{static_cast<int>(impl_from_env())};
+
+thread_local int t_last_hip_error = 0;
+
+void add_counters(ar_collective_t coll, const std::vector<ar::Step>& sched, int n, size_t isz) {
+  uint64_t sent[AR_MAX_RANKS] = {};
+  uint64_t recv[AR_MAX_RANKS] = {};
+  ar::count_bytes(sched, isz, sent, recv);
+  std::lock_guard<std::mutex> lock(g_counter_mu);
+  for (int r = 0; r < n; ++r) {
+    g_sent[r] += sent[r];
+    g_recv[r] += recv[r];
+  }
+  g_steps += static_cast<uint64_t>(ar::expected_steps(coll, n));
+}
+
+ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar_dtype_t dtype,
+                int op, int root, void* stream_ptr) {
+  const ar_status_t v = ar::validate(bufs, n, count, static_cast<int>(dtype), op, root);
+  if (v != AR_SUCCESS) return v;
+  const ar_op_t aop = op >= 0 ? static_cast<ar_op_t>(op) : AR_SUM;
+  const std::vector<ar::Step> sched = ar::schedule_for(coll, n, count, root < 0 ? 0 : root);
+  if (n == 1 || count == 0) {
+    add_counters(coll, sched, n, ar::itemsize(dtype));
+    return AR_SUCCESS;
+  }
+
+  ar::RankPtrs ptrs;
+  std::memset(&ptrs, 0, sizeof(ptrs));
+  bool aligned16 = true;
+  for (int r = 0; r < n; ++r) {
+    ptrs.p[r] = bufs[r];
+    aligned16 = aligned16 && (reinterpret_cast<uintptr_t>(bufs[r]) % 16 == 0);
+  }
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const ar_impl_t impl = static_cast<ar_impl_t>(g_impl.load());
+
+  // The kernels move 16-byte packs at element indices that are multiples of
+  // the pack width, which needs every buffer 16-byte aligned.  Buffers that
+  // are only element-aligned are not supported by this build.
+  if (!aligned16) return AR_ERROR_UNSUPPORTED;
+
+  hipError_t err = hipSuccess;
+  if (impl == AR_IMPL_STEP) {
+    for (const ar::Step& s : sched) {
+      err = ar::launch_step(ptrs, s, dtype, aop, stream);
+      if (err != hipSuccess) break;
+    }
+  } else {
+    switch (coll) {
+      case AR_RING_ALLREDUCE:
+        err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, true, stream);
+        break;
+      case AR_REDUCE_SCATTER:
+        err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, stream);
+        break;
+      case AR_ALLGATHER:
+        err = ar::launch_fanout(ptrs, n, count, dtype, false, 0, stream);
+        break;
+      case AR_BROADCAST:
+        err = ar::launch_fanout(ptrs, n, count, dtype, true, root, stream);
+        break;
+      case AR_TREE_ALLREDUCE:
+        err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, stream);
+        break;
+    }
+  }
+  if (err != hipSuccess) {
+    t_last_hip_error = static_cast<int>(err);
+    return AR_ERROR_HIP;
+  }
+  add_counters(coll, sched, n, ar::itemsize(dtype));
+  return AR_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                              ar_op_t op, void* stream) {
+  if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
+  return run(AR_RING_ALLREDUCE, bufs, nranks, count, dtype, static_cast<int>(op), -1, stream);
+}
+
+ar_status_t ar_reduce_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                              ar_op_t op, void* stream) {
+  if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
+  return run(AR_REDUCE_SCATTER, bufs, nranks, count, dtype, static_cast<int>(op), -1, stream);
+}
+
+ar_status_t ar_allgather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                         void* stream) {
+  return run(AR_ALLGATHER, bufs, nranks, count, dtype, -1, -1, stream);
+}
+
+ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
+                         void* stream) {
+  if (root < 0) return AR_ERROR_INVALID_ARGUMENT;
+  return run(AR_BROADCAST, bufs, nranks, count, dtype, -1, root, stream);
+}
+
+ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                              ar_op_t op, void* stream) {
+  if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
+  return run(AR_TREE_ALLREDUCE, bufs, nranks, count, dtype, static_cast<int>(op), -1, stream);
+}
+
+size_t ar_chunk_size(int nranks, size_t count) {
+  return static_cast<size_t>(ar::chunk_size(nranks, count));
+}
+
+ar_status_t ar_chunk_range(int nranks, size_t count, int chunk, size_t* begin, size_t* end) {
+  if (nranks < 1 || nranks > AR_MAX_RANKS || chunk < 0 || chunk >= nranks || begin == nullptr ||
+      end == nullptr)
+    return AR_ERROR_INVALID_ARGUMENT;
+  uint64_t lo, hi;
+  ar::chunk_bounds(nranks, count, chunk, &lo, &hi);
+  *begin = static_cast<size_t>(lo);
+  *end = static_cast<size_t>(hi);
+  return AR_SUCCESS;
+}
+
+ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype,
+                              int root, uint64_t* sent, uint64_t* recv) {
+  if (nranks < 1 || nranks > AR_MAX_RANKS || !ar::dtype_ok(static_cast<int>(dtype)) ||
+      sent == nullptr || recv == nullptr || ar::expected_steps(coll, nranks) < 0)
+    return AR_ERROR_INVALID_ARGUMENT;
+  if (coll == AR_BROADCAST && (root < 0 || root >= nranks)) return AR_ERROR_INVALID_ARGUMENT;
+  for (int r = 0; r < nranks; ++r) sent[r] = recv[r] = 0;
+  const std::vector<ar::Step> sched =
+      ar::schedule_for(coll, nranks, count, coll == AR_BROADCAST ? root : 0);
+  ar::count_bytes(sched, ar::itemsize(dtype), sent, recv);
+  return AR_SUCCESS;
+}
+
+int ar_expected_steps(ar_collective_t coll, int nranks) { return ar::expected_steps(coll, nranks); }
+
+ar_status_t ar_counters_read(int nranks, uint64_t* sent, uint64_t* recv, uint64_t* steps) {
+  if (nranks < 0 || nranks > AR_MAX_RANKS) return AR_ERROR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lock(g_counter_mu);
+  for (int r = 0; r < nranks; ++r) {
+    if (sent != nullptr) sent[r] = g_sent[r];
+    if (recv != nullptr) recv[r] = g_recv[r];
+  }
+  if (steps != nullptr) *steps = g_steps;
+  return AR_SUCCESS;
+}
+
+void ar_counters_reset(void) {
+  std::lock_guard<std::mutex> lock(g_counter_mu);
+  for (int r = 0; r < AR_MAX_RANKS; ++r) g_sent[r] = g_recv[r] = 0;
+  g_steps = 0;
+}
+
+ar_status_t ar_set_impl(ar_impl_t impl) {
+  if (impl != AR_IMPL_FUSED && impl != AR_IMPL_STEP) return AR_ERROR_INVALID_ARGUMENT;
+  g_impl.store(static_cast<int>(impl));
+  return AR_SUCCESS;
+}
+
+ar_impl_t ar_get_impl(void) { return static_cast<ar_impl_t>(g_impl.load()); }
+
+const char* ar_status_string(ar_status_t status) {
+  switch (status) {
+    case AR_SUCCESS: return "success";
+    case AR_ERROR_INVALID_ARGUMENT: return "invalid argument";
+    case AR_ERROR_UNSUPPORTED: return "unsupported";
+    case AR_ERROR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int ar_last_hip_error(void) { return t_last_hip_error; }
+
+int ar_version(void) { return AR_VERSION; }
+
+}  // extern "C"

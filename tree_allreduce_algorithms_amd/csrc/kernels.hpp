@@ -1,0 +1,39 @@
+// Kernel launchers for the collectives (gfx950).  Every launcher enqueues on
+// `stream` and returns the hipError_t of the launch; none synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ar.h"
+#include "plan.hpp"
+
+namespace ar {
+
+struct RankPtrs {
+  void* p[AR_MAX_RANKS];
+};
+
+// Fused ring fold: for every element i of chunk c, fold ranks c+1, c+2, ...,
+// c in that order (each hop: rank's own value (+) incoming partial) and store
+// the result into every rank (all_ranks, AllReduce) or into rank c only
+// (ReduceScatter).
+hipError_t launch_ring_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                            ar_op_t op, bool all_ranks, hipStream_t stream);
+
+// Fused fan-out copy: for every element i of chunk c, copy from rank c
+// (allgather) or from `root` (broadcast) into every other rank.
+hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                         bool from_root, int root, hipStream_t stream);
+
+// Fused double binomial tree: per element, the pairwise fold of the tree that
+// owns it, stored into every rank.
+hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                            ar_op_t op, hipStream_t stream);
+
+// One schedule step: all of its transfers in one launch.
+hipError_t launch_step(const RankPtrs& ptrs, const Step& step, ar_dtype_t dtype, ar_op_t op,
+                       hipStream_t stream);
+
+}  // namespace ar

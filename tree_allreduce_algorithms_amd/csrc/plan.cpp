@@ -1,0 +1,173 @@
+// Host-side planning: validation, chunk layout, logical schedules, counters.
+//
+// Schedules follow "Collectives from scratch" (从零实现集合通信), section
+// "two-pass ring allreduce": rank r sends to r+1; the ReduceScatter pass has
+// rank r forward chunk (r - s) mod N at step s = 1..N-1 (so rank r finishes
+// owning chunk r), the AllGather pass forwards the completed chunks around
+// once more.  The tree follows Lecture 09 section 5.2 and Chapter 4 section
+// 4.3.2 (two trees, half the data each), read as two binomial trees, the
+// second on mirrored roles.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <utility>
+
+namespace ar {
+
+size_t itemsize(ar_dtype_t dtype) { return dtype == AR_BFLOAT16 ? 2 : 4; }
+
+bool dtype_ok(int dtype) { return dtype == AR_INT32 || dtype == AR_FLOAT32 || dtype == AR_BFLOAT16; }
+
+bool op_ok(int op) { return op == AR_SUM || op == AR_PROD || op == AR_MAX || op == AR_MIN; }
+
+uint64_t chunk_size(int n, uint64_t count) {
+  if (n < 1) return 0;
+  const uint64_t un = static_cast<uint64_t>(n);
+  return count / un + (count % un != 0 ? 1 : 0);
+}
+
+void chunk_bounds(int n, uint64_t count, int c, uint64_t* lo, uint64_t* hi) {
+  const uint64_t size = chunk_size(n, count);
+  const uint64_t a = static_cast<uint64_t>(c) * size;
+  *lo = std::min(a, count);
+  *hi = std::min(a + size, count);
+}
+
+int tree_depth(int n) {
+  int d = 0;
+  while ((1 << d) < n) ++d;
+  return d;
+}
+
+uint64_t tree_split(uint64_t count) { return count / 2 + (count % 2); }
+
+std::vector<Step> ring_reduce_scatter_schedule(int n, uint64_t count) {
+  std::vector<Step> out;
+  for (int t = 0; t + 1 < n; ++t) {
+    Step s{true, {}};
+    for (int r = 0; r < n; ++r) {
+      const int c = ((r - t - 1) % n + n) % n;
+      uint64_t lo, hi;
+      chunk_bounds(n, count, c, &lo, &hi);
+      s.xfers.push_back({r, (r + 1) % n, lo, hi});
+    }
+    out.push_back(std::move(s));
+  }
+  return out;
+}
+
+std::vector<Step> ring_allgather_schedule(int n, uint64_t count) {
+  std::vector<Step> out;
+  for (int t = 0; t + 1 < n; ++t) {
+    Step s{false, {}};
+    for (int r = 0; r < n; ++r) {
+      const int c = ((r - t) % n + n) % n;
+      uint64_t lo, hi;
+      chunk_bounds(n, count, c, &lo, &hi);
+      s.xfers.push_back({r, (r + 1) % n, lo, hi});
+    }
+    out.push_back(std::move(s));
+  }
+  return out;
+}
+
+std::vector<Step> tree_allreduce_schedule(int n, uint64_t count) {
+  const int depth = tree_depth(n);
+  const uint64_t h = tree_split(count);
+  const uint64_t seg_lo[2] = {0, h};
+  const uint64_t seg_hi[2] = {h, count};
+  std::vector<Step> out;
+  for (int k = 0; k < depth; ++k) {            // reduce rounds, leaves first
+    const int stride = 1 << k;
+    Step s{true, {}};
+    for (int tree = 0; tree < 2; ++tree)
+      for (int q = 0; q + stride < n; q += 2 * stride)
+        s.xfers.push_back({tree_rank(tree, q + stride, n), tree_rank(tree, q, n), seg_lo[tree],
+                           seg_hi[tree]});
+    out.push_back(std::move(s));
+  }
+  for (int k = depth - 1; k >= 0; --k) {       // broadcast rounds, root first
+    const int stride = 1 << k;
+    Step s{false, {}};
+    for (int tree = 0; tree < 2; ++tree)
+      for (int q = 0; q + stride < n; q += 2 * stride)
+        s.xfers.push_back({tree_rank(tree, q, n), tree_rank(tree, q + stride, n), seg_lo[tree],
+                           seg_hi[tree]});
+    out.push_back(std::move(s));
+  }
+  return out;
+}
+
+std::vector<Step> broadcast_schedule(int n, uint64_t count, int root) {
+  std::vector<Step> out;
+  for (int k = tree_depth(n) - 1; k >= 0; --k) {
+    const int stride = 1 << k;
+    Step s{false, {}};
+    for (int q = 0; q + stride < n; q += 2 * stride)
+      s.xfers.push_back({(q + root) % n, (q + stride + root) % n, 0, count});
+    out.push_back(std::move(s));
+  }
+  return out;
+}
+
+std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int root) {
+  switch (coll) {
+    case AR_RING_ALLREDUCE: {
+      std::vector<Step> a = ring_reduce_scatter_schedule(n, count);
+      std::vector<Step> b = ring_allgather_schedule(n, count);
+      a.insert(a.end(), b.begin(), b.end());
+      return a;
+    }
+    case AR_REDUCE_SCATTER: return ring_reduce_scatter_schedule(n, count);
+    case AR_ALLGATHER: return ring_allgather_schedule(n, count);
+    case AR_BROADCAST: return broadcast_schedule(n, count, root);
+    case AR_TREE_ALLREDUCE: return tree_allreduce_schedule(n, count);
+  }
+  return {};
+}
+
+void count_bytes(const std::vector<Step>& steps, size_t isz, uint64_t* sent, uint64_t* recv) {
+  for (const Step& s : steps)
+    for (const Transfer& x : s.xfers) {
+      const uint64_t b = (x.hi - x.lo) * isz;
+      sent[x.src] += b;
+      recv[x.dst] += b;
+    }
+}
+
+int expected_steps(ar_collective_t coll, int n) {
+  if (n < 1 || n > AR_MAX_RANKS) return -1;
+  switch (coll) {
+    case AR_RING_ALLREDUCE: return 2 * (n - 1);
+    case AR_REDUCE_SCATTER:
+    case AR_ALLGATHER: return n - 1;
+    case AR_BROADCAST: return tree_depth(n);
+    case AR_TREE_ALLREDUCE: return 2 * tree_depth(n);
+  }
+  return -1;
+}
+
+ar_status_t validate(void* const* bufs, int n, size_t count, int dtype, int op, int root) {
+  if (!dtype_ok(dtype)) return AR_ERROR_INVALID_ARGUMENT;
+  if (op >= 0 && !op_ok(op)) return AR_ERROR_INVALID_ARGUMENT;
+  if (bufs == nullptr || n < 1 || n > AR_MAX_RANKS) return AR_ERROR_INVALID_ARGUMENT;
+  if (root >= n) return AR_ERROR_INVALID_ARGUMENT;
+  const size_t isz = itemsize(static_cast<ar_dtype_t>(dtype));
+  if (count > SIZE_MAX / isz) return AR_ERROR_INVALID_ARGUMENT;
+  const uint64_t bytes = static_cast<uint64_t>(count) * isz;
+  std::pair<uintptr_t, int> order[AR_MAX_RANKS];
+  for (int r = 0; r < n; ++r) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(bufs[r]);
+    if (p == 0 || p % isz != 0) return AR_ERROR_INVALID_ARGUMENT;
+    if (bytes > UINTPTR_MAX - p) return AR_ERROR_INVALID_ARGUMENT;
+    order[r] = {p, r};
+  }
+  if (bytes > 0) {
+    std::sort(order, order + n);
+    for (int i = 0; i + 1 < n; ++i)
+      if (order[i].first + bytes > order[i + 1].first) return AR_ERROR_INVALID_ARGUMENT;
+  }
+  return AR_SUCCESS;
+}
+
+}  // namespace ar

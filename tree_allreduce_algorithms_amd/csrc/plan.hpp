@@ -1,0 +1,64 @@
+// Host-side planning for the collectives: argument validation, the chunk
+// layout and the logical schedules (which rank sends which element range to
+// which rank at each step).  Pure C++, no HIP: it runs without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "ar.h"
+
+namespace ar {
+
+// One logical transfer inside a step: elements [lo, hi) of rank `src` go to
+// rank `dst`, which either combines them into its own copy (reduce steps) or
+// overwrites its copy (copy steps).
+struct Transfer {
+  int src;
+  int dst;
+  uint64_t lo;
+  uint64_t hi;
+};
+
+struct Step {
+  bool reduce;                   // true: dst = dst (+) src; false: dst = src
+  std::vector<Transfer> xfers;   // disjoint destinations within a step
+};
+
+size_t itemsize(ar_dtype_t dtype);
+bool dtype_ok(int dtype);
+bool op_ok(int op);
+
+// Ring chunks: C = ceil(T/N); chunk c = [min(cC, T), min((c+1)C, T)).
+uint64_t chunk_size(int n, uint64_t count);
+void chunk_bounds(int n, uint64_t count, int c, uint64_t* lo, uint64_t* hi);
+
+// Binomial tree depth ceil(log2 n).
+int tree_depth(int n);
+
+// Double-tree split: tree 0 owns [0, h), tree 1 owns [h, T), h = ceil(T/2).
+uint64_t tree_split(uint64_t count);
+// Rank that plays `role` in tree 0 (identity) or tree 1 (mirror).
+inline int tree_rank(int tree, int role, int n) { return tree == 0 ? role : n - 1 - role; }
+
+// Logical schedules.  A ring AllReduce is the ReduceScatter steps followed by
+// the AllGather steps; the tree is its reduce rounds then its broadcast rounds.
+std::vector<Step> ring_reduce_scatter_schedule(int n, uint64_t count);
+std::vector<Step> ring_allgather_schedule(int n, uint64_t count);
+std::vector<Step> tree_allreduce_schedule(int n, uint64_t count);
+std::vector<Step> broadcast_schedule(int n, uint64_t count, int root);
+std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int root);
+
+// Adds the bytes of every transfer to sent[src] / recv[dst].
+void count_bytes(const std::vector<Step>& steps, size_t isz, uint64_t* sent, uint64_t* recv);
+
+int expected_steps(ar_collective_t coll, int n);
+
+// Validation shared by every collective call.  `op` < 0 means "not used",
+// `root` < 0 means "not used".  Checks: bufs / entries non-NULL, n in range,
+// element alignment, count * itemsize overflow, pairwise overlap of the
+// [ptr, ptr + count * itemsize) ranges, dtype / op / root ranges.
+ar_status_t validate(void* const* bufs, int n, size_t count, int dtype, int op, int root);
+
+}  // namespace ar
