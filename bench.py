@@ -61,10 +61,13 @@ def parse():
 
 
 def kernel_source_hash():
+    """sha256 over every device-code source of the library (sorted by name)."""
+    csrc = os.path.join(ROOT, "tree_allreduce_algorithms_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("kernels.hip", "kernels.hpp"):
-        with open(os.path.join(ROOT, "tree_allreduce_algorithms_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 

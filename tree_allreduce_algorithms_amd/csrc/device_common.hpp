@@ -1,0 +1,320 @@
+// Device-side building blocks shared by the collective kernels (gfx950).
+//
+// All of the work is streaming: every kernel reads each input element once
+// and writes each output element once, so HBM bandwidth bounds everything and
+// no matrix cores are involved.  Common structure:
+//
+// * A kernel processes "segments" (a ring chunk, a tree's half, a transfer's
+//   element range), one per blockIdx.y.  Within a segment, elements are
+//   grouped into 16-byte packs aligned to the element index (every rank
+//   buffer is 16-byte aligned when these kernels run, so a pack maps to one
+//   dwordx4 access in every buffer).  Packs are split into tiles of
+//   kBlock * U packs; a block walks tiles blockIdx.x, blockIdx.x + gridDim.x,
+//   ...  The unaligned head and tail of a segment (fewer than one pack each)
+//   are handled element by element by block x == 0.
+// * Everything about which rank to read or write is uniform per block (the
+//   segment fixes it).  A tile's byte offset is uniform too, so rank pointer
+//   plus tile offset sits in scalar registers and each lane adds only a
+//   32-bit offset below 64 KiB: one VGPR of addressing per pack instead of a
+//   64-bit address per (rank, pack).
+// * Each element is owned by exactly one thread, which reads all the values
+//   it needs before writing any of them, so the in-place updates never race.
+//
+// Arithmetic of one hop is `local (+) incoming` at the receiving rank
+// (Lecture 09 section 7.1 and Chapter 4 section 4.3.1 update the receiver's
+// own chunk in place): int32 wraps, float32 is one IEEE operation (built with
+// -ffp-contract=off, subnormals kept), bfloat16 widens to float32, applies
+// the operation and rounds back to nearest-even after every hop.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+
+#include "kernels.hpp"
+
+namespace ar {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr uint32_t kMaxGridX = 1u << 22;   // grid-stride loops cover any excess
+
+template <ar_dtype_t DT> struct Elem;
+template <> struct Elem<AR_INT32> { using T = int32_t; };
+template <> struct Elem<AR_FLOAT32> { using T = float; };
+template <> struct Elem<AR_BFLOAT16> { using T = uint16_t; };
+
+__device__ __forceinline__ float bf16_widen(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16 bits, round to nearest, ties to even.  gfx950 converts
+// in one instruction (v_cvt_pk_bf16_f32, which rounds by the current mode:
+// nearest-even).
+__device__ __forceinline__ uint16_t bf16_round(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+using F32x2 = float __attribute__((ext_vector_type(2)));
+using BF16x2 = __bf16 __attribute__((ext_vector_type(2)));
+
+// Two float32 values -> two bfloat16 in one 32-bit word (lo in bits 0-15).
+__device__ __forceinline__ uint32_t bf16x2_round(float lo, float hi) {
+  const F32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, BF16x2));
+}
+
+template <ar_dtype_t DT, ar_op_t OP> struct Combine;
+
+template <ar_op_t OP> struct Combine<AR_INT32, OP> {
+  static __device__ __forceinline__ int32_t apply(int32_t local, int32_t in) {
+    if constexpr (OP == AR_SUM)
+      return static_cast<int32_t>(static_cast<uint32_t>(local) + static_cast<uint32_t>(in));
+    else if constexpr (OP == AR_PROD)
+      return static_cast<int32_t>(static_cast<uint32_t>(local) * static_cast<uint32_t>(in));
+    else if constexpr (OP == AR_MAX)
+      return in > local ? in : local;
+    else
+      return in < local ? in : local;
+  }
+};
+
+template <ar_op_t OP> struct Combine<AR_FLOAT32, OP> {
+  static __device__ __forceinline__ float apply(float local, float in) {
+    if constexpr (OP == AR_SUM)
+      return local + in;
+    else if constexpr (OP == AR_PROD)
+      return local * in;
+    else if constexpr (OP == AR_MAX)
+      return in > local ? in : local;
+    else
+      return in < local ? in : local;
+  }
+};
+
+template <ar_op_t OP> struct Combine<AR_BFLOAT16, OP> {
+  static __device__ __forceinline__ uint16_t apply(uint16_t local, uint16_t in) {
+    const float a = bf16_widen(local);
+    const float b = bf16_widen(in);
+    if constexpr (OP == AR_SUM)
+      return bf16_round(a + b);
+    else if constexpr (OP == AR_PROD)
+      return bf16_round(a * b);
+    else if constexpr (OP == AR_MAX)
+      return b > a ? in : local;
+    else
+      return b < a ? in : local;
+  }
+};
+
+// K elements moved as one aligned access (K * sizeof(T) == 16 -> dwordx4).
+template <class T, int K> struct alignas(sizeof(T) * K) Pack {
+  T e[K];
+};
+
+template <int W> struct Words {
+  uint32_t w[W];
+};
+
+template <ar_dtype_t DT, ar_op_t OP, class T, int K>
+__device__ __forceinline__ Pack<T, K> combine(const Pack<T, K>& local, const Pack<T, K>& in) {
+  if constexpr (DT == AR_BFLOAT16 && (OP == AR_SUM || OP == AR_PROD) && K % 2 == 0) {
+    // Two bfloat16 per 32-bit word: widening is a shift (low half) or a mask
+    // (high half), and one conversion rounds both results.
+    const Words<K / 2> lw = __builtin_bit_cast(Words<K / 2>, local);
+    const Words<K / 2> iw = __builtin_bit_cast(Words<K / 2>, in);
+    Words<K / 2> r;
+#pragma unroll
+    for (int j = 0; j < K / 2; ++j) {
+      const float a0 = __uint_as_float(lw.w[j] << 16);
+      const float a1 = __uint_as_float(lw.w[j] & 0xffff0000u);
+      const float b0 = __uint_as_float(iw.w[j] << 16);
+      const float b1 = __uint_as_float(iw.w[j] & 0xffff0000u);
+      if constexpr (OP == AR_SUM)
+        r.w[j] = bf16x2_round(a0 + b0, a1 + b1);
+      else
+        r.w[j] = bf16x2_round(a0 * b0, a1 * b1);
+    }
+    return __builtin_bit_cast(Pack<T, K>, r);
+  } else {
+    Pack<T, K> r;
+#pragma unroll
+    for (int j = 0; j < K; ++j) r.e[j] = Combine<DT, OP>::apply(local.e[j], in.e[j]);
+    return r;
+  }
+}
+
+// Plain element accesses (the unaligned head and tail of a segment).
+template <class P> __device__ __forceinline__ P load(const void* base, uint64_t i) {
+  return reinterpret_cast<const P*>(base)[i];
+}
+template <class P> __device__ __forceinline__ void store(void* base, uint64_t i, const P& v) {
+  reinterpret_cast<P*>(base)[i] = v;
+}
+
+// Streaming 16-byte accesses for the pack paths.  A collective touches every
+// byte of every rank buffer once (a read, a write, or a read then a write by
+// the same thread), so there is no reuse for L2 to capture; the non-temporal
+// hint lets the loads and stores stream past it.  Measured on gfx950 with
+// 8 x 1.2 GB buffers, the hint raises a pure read stream from about 6.4 to
+// 7.0 TB/s and the 8-rank fold from about 5.2 to 5.5 TB/s.
+using Raw16 = uint32_t __attribute__((ext_vector_type(4)));
+
+// `base` is uniform (rank pointer + tile offset); `off` is the lane's byte
+// offset inside the tile.
+__device__ __forceinline__ const char* at(const void* p, uint64_t byte_off) {
+  return static_cast<const char*>(p) + byte_off;
+}
+__device__ __forceinline__ char* at(void* p, uint64_t byte_off) {
+  return static_cast<char*>(p) + byte_off;
+}
+
+template <class P> __device__ __forceinline__ P load_stream(const char* base, uint32_t off) {
+  static_assert(sizeof(P) == 16, "streaming accesses move 16-byte packs");
+  const Raw16 v = __builtin_nontemporal_load(reinterpret_cast<const Raw16*>(base + off));
+  return __builtin_bit_cast(P, v);
+}
+template <class P>
+__device__ __forceinline__ void store_stream(char* base, uint32_t off, const P& v) {
+  static_assert(sizeof(P) == 16, "streaming accesses move 16-byte packs");
+  __builtin_nontemporal_store(__builtin_bit_cast(Raw16, v), reinterpret_cast<Raw16*>(base + off));
+}
+
+// Elements [lo, hi) of a segment split into an element-wise head, whole
+// K-element packs [plo, phi) and an element-wise tail.
+struct Span {
+  uint64_t lo, hi, plo, phi, head_end, tail_begin;
+  __device__ uint32_t scalar_count() const {
+    return static_cast<uint32_t>((head_end - lo) + (hi - tail_begin));
+  }
+  __device__ uint64_t scalar_index(uint32_t t) const {
+    const uint32_t head = static_cast<uint32_t>(head_end - lo);
+    return t < head ? lo + t : tail_begin + (t - head);
+  }
+};
+
+template <int K> __device__ __forceinline__ Span make_span(uint64_t lo, uint64_t hi) {
+  Span s;
+  s.lo = lo;
+  s.hi = hi;
+  s.plo = (lo + K - 1) / K;
+  const uint64_t ph = hi / K;
+  s.phi = ph > s.plo ? ph : s.plo;
+  s.head_end = hi < s.plo * K ? hi : s.plo * K;
+  const uint64_t tb = s.phi * K > s.head_end ? s.phi * K : s.head_end;
+  s.tail_begin = tb < hi ? tb : hi;
+  return s;
+}
+
+// Tiles lie on a grid of kBlock * U packs anchored at element 0 of the
+// buffer, not at the segment's start: tile t covers packs [t*TP, (t+1)*TP).
+// When a segment starts mid-line (a ragged chunk, the second tree half) its
+// first and last tiles are partly masked, but every wave still writes whole,
+// line-aligned 1 KiB runs.  Anchoring tiles at the segment start instead
+// shifts every store off the 128-byte lines, so neighbouring waves each write
+// half of the same lines; with streaming stores that measured about 25 % slower
+// on a 64-rank AllGather.
+template <int U> struct TileGrid {
+  static constexpr uint64_t kPacks = static_cast<uint64_t>(kBlock) * U;
+  // First pack of the segment's `tile`-th tile (tile counts from the tile
+  // holding the segment's first pack).
+  static __device__ __forceinline__ uint64_t first_pack(uint64_t plo, uint64_t tile) {
+    return (plo / kPacks + tile) * kPacks;
+  }
+};
+
+// Per-tile lane setup: live[u] says whether the lane's pack u lies inside the
+// segment's packs [plo, phi), off[u] is its byte offset inside the tile.
+template <int U> struct TileLanes {
+  bool live[U];
+  uint32_t off[U];
+  __device__ TileLanes(uint64_t tile_pack, uint64_t plo, uint64_t phi) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t lane_pack = threadIdx.x + static_cast<uint32_t>(u * kBlock);
+      const uint64_t p = tile_pack + lane_pack;
+      live[u] = p >= plo && p < phi;
+      off[u] = lane_pack * 16u;
+    }
+  }
+};
+
+__device__ __forceinline__ int wrap_rank(int r, int n) { return r >= n ? r - n : r; }
+
+__device__ __forceinline__ uint64_t umin(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers.
+// ---------------------------------------------------------------------------
+// Upper bound on the tiles of the buffer-anchored grid that one segment of
+// at most max_elems elements touches (its packs plus one partial tile at each
+// end).
+inline uint64_t tiles_for(uint64_t max_elems, int pack, int unroll) {
+  const uint64_t packs = max_elems / pack + 1;
+  const uint64_t per_tile = static_cast<uint64_t>(kBlock) * unroll;
+  return (packs + per_tile - 1) / per_tile + 1;
+}
+
+// Packs per lane per tile for a kernel over N ranks.  A tile moves about
+// (N reads + N writes) * U * 4 KiB per block, so the unroll shrinks as N grows
+// to keep blocks short enough that the last ones do not leave most of the chip
+// idle.  AR_TUNE_UNROLL (1, 2 or 4), read at the first launch, overrides the
+// choice for measurements; it changes nothing but the pack grouping, never
+// any element's arithmetic.
+inline int pick_unroll(int n) {
+  static const int forced = [] {
+    const char* v = std::getenv("AR_TUNE_UNROLL");
+    const int u = v != nullptr ? std::atoi(v) : 0;
+    return (u == 1 || u == 2 || u == 4) ? u : 0;
+  }();
+  if (forced != 0) return forced;
+  return n <= 8 ? 4 : (n <= 16 ? 2 : 1);
+}
+
+inline uint32_t grid_x(uint64_t tiles) {
+  return static_cast<uint32_t>(std::min<uint64_t>(tiles, kMaxGridX));
+}
+
+template <class Args>
+hipError_t launch(const void* fn, dim3 grid, const Args& args, hipStream_t stream) {
+  Args copy = args;
+  void* kargs[] = {&copy};
+  return hipLaunchKernel(fn, grid, dim3(kBlock), kargs, 0, stream);
+}
+
+// dtype x op dispatch onto a template taking <ar_dtype_t, ar_op_t>.
+#define AR_DISPATCH(FN, DTYPE, OP, ...)                                          \
+  do {                                                                            \
+    switch (DTYPE) {                                                              \
+      case AR_INT32:                                                              \
+        switch (OP) {                                                             \
+          case AR_SUM: return FN<AR_INT32, AR_SUM>(__VA_ARGS__);                  \
+          case AR_PROD: return FN<AR_INT32, AR_PROD>(__VA_ARGS__);                \
+          case AR_MAX: return FN<AR_INT32, AR_MAX>(__VA_ARGS__);                  \
+          case AR_MIN: return FN<AR_INT32, AR_MIN>(__VA_ARGS__);                  \
+        }                                                                         \
+        break;                                                                    \
+      case AR_FLOAT32:                                                            \
+        switch (OP) {                                                             \
+          case AR_SUM: return FN<AR_FLOAT32, AR_SUM>(__VA_ARGS__);                \
+          case AR_PROD: return FN<AR_FLOAT32, AR_PROD>(__VA_ARGS__);              \
+          case AR_MAX: return FN<AR_FLOAT32, AR_MAX>(__VA_ARGS__);                \
+          case AR_MIN: return FN<AR_FLOAT32, AR_MIN>(__VA_ARGS__);                \
+        }                                                                         \
+        break;                                                                    \
+      case AR_BFLOAT16:                                                           \
+        switch (OP) {                                                             \
+          case AR_SUM: return FN<AR_BFLOAT16, AR_SUM>(__VA_ARGS__);               \
+          case AR_PROD: return FN<AR_BFLOAT16, AR_PROD>(__VA_ARGS__);             \
+          case AR_MAX: return FN<AR_BFLOAT16, AR_MAX>(__VA_ARGS__);               \
+          case AR_MIN: return FN<AR_BFLOAT16, AR_MIN>(__VA_ARGS__);               \
+        }                                                                         \
+        break;                                                                    \
+    }                                                                             \
+    return hipErrorInvalidValue;                                                  \
+  } while (0)
+
+}  // namespace
+}  // namespace ar

@@ -1,0 +1,127 @@
+// Fused ring fold (ReduceScatter / AllReduce in one pass), gfx950.
+//
+// For chunk c the ring's ReduceScatter pass starts with rank c+1's value and
+// has ranks c+2, ..., c each add their own value to the incoming partial, rank
+// c finishing the sum ("Collectives from scratch", two-pass ring: rank r ends
+// up owning chunk r).  Doing those N-1 hops for one element in registers
+// gives bit-for-bit the value the step-by-step ring leaves in rank c; the
+// AllGather pass then only copies it, so AllReduce stores it in every rank.
+#include "device_common.hpp"
+
+namespace ar {
+namespace {
+
+constexpr int kFoldBatch = 8;   // rank loads issued before folding them
+
+struct FoldArgs {
+  RankPtrs ptrs;
+  uint64_t count;
+  uint64_t chunk;
+  uint64_t tiles;
+  int n;
+};
+
+// U: packs per lane per tile.  ALL: store into every rank (AllReduce) or only
+// into the chunk's owner (ReduceScatter).
+template <ar_dtype_t DT, ar_op_t OP, bool ALL, int U>
+__global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
+  using T = typename Elem<DT>::T;
+  constexpr int K = 16 / sizeof(T);
+  constexpr int B = kFoldBatch;
+  using P = Pack<T, K>;
+  using S = Pack<T, 1>;
+
+  const int n = a.n;
+  const int c = blockIdx.y;
+  const uint64_t lo = umin(static_cast<uint64_t>(c) * a.chunk, a.count);
+  const uint64_t hi = umin(lo + a.chunk, a.count);
+  if (lo >= hi) return;
+  const int first = wrap_rank(c + 1, n);
+  const Span s = make_span<K>(lo, hi);
+
+  for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+    const uint64_t tp = TileGrid<U>::first_pack(s.plo, tile);
+    if (tp >= s.phi) break;
+    const uint64_t toff = tp * 16;
+    const TileLanes<U> ln(tp, s.plo, s.phi);
+
+    P acc[U];
+    for (int k0 = 0; k0 < n; k0 += B) {
+      P in[B][U];
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (k0 + j < n) {
+          const char* src = at(a.ptrs.p[wrap_rank(first + k0 + j, n)], toff);
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (ln.live[u]) in[j][u] = load_stream<P>(src, ln.off[u]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (k0 + j < n) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            acc[u] = (k0 + j == 0) ? in[j][u] : combine<DT, OP>(in[j][u], acc[u]);
+        }
+      }
+    }
+    if (ALL) {
+      for (int r = 0; r < n; ++r) {
+        char* dst = at(a.ptrs.p[r], toff);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (ln.live[u]) store_stream<P>(dst, ln.off[u], acc[u]);
+      }
+    } else {
+      char* dst = at(a.ptrs.p[c], toff);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ln.live[u]) store_stream<P>(dst, ln.off[u], acc[u]);
+    }
+  }
+
+  if (blockIdx.x == 0 && threadIdx.x < s.scalar_count()) {
+    const uint64_t e = s.scalar_index(threadIdx.x);
+    S acc = load<S>(a.ptrs.p[first], e);
+    for (int k = 1; k < n; ++k)
+      acc = combine<DT, OP>(load<S>(a.ptrs.p[wrap_rank(first + k, n)], e), acc);
+    if (ALL) {
+      for (int r = 0; r < n; ++r) store<S>(a.ptrs.p[r], e, acc);
+    } else {
+      store<S>(a.ptrs.p[c], e, acc);
+    }
+  }
+}
+
+template <ar_dtype_t DT, ar_op_t OP, bool ALL>
+const void* ring_fold_fn(int u) {
+  if (u == 4) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 4>);
+  if (u == 2) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 2>);
+  return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 1>);
+}
+
+template <ar_dtype_t DT, ar_op_t OP>
+hipError_t ring_fold_typed(FoldArgs a, bool all, hipStream_t stream) {
+  constexpr int K = 16 / sizeof(typename Elem<DT>::T);
+  const int u = pick_unroll(a.n);
+  a.tiles = tiles_for(a.chunk, K, u);
+  const dim3 grid(grid_x(a.tiles), a.n);
+  return launch(all ? ring_fold_fn<DT, OP, true>(u) : ring_fold_fn<DT, OP, false>(u), grid, a,
+                stream);
+}
+
+}  // namespace
+
+hipError_t launch_ring_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                            ar_op_t op, bool all_ranks, hipStream_t stream) {
+  FoldArgs a;
+  a.ptrs = ptrs;
+  a.count = count;
+  a.chunk = chunk_size(n, count);
+  a.n = n;
+  a.tiles = 0;
+  AR_DISPATCH(ring_fold_typed, dtype, op, a, all_ranks, stream);
+}
+
+}  // namespace ar

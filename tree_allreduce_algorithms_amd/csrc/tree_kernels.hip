@@ -1,0 +1,168 @@
+// Fused double binomial tree AllReduce (gfx950).
+#include "device_common.hpp"
+
+namespace ar {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Fused double binomial tree.  Tree 0 owns [0, half) with role == rank, tree 1
+// owns [half, count) with role == N-1-rank.  Reduce round k combines role q
+// (q mod 2^(k+1) == 0) with role q + 2^k when that role exists: role q keeps
+// own (+) incoming.  Doing every round in registers leaves role 0's value,
+// which the broadcast rounds would copy to every rank.
+//
+// The rounds are evaluated while streaming the roles in order 0, 1, ..., N-1,
+// like a binary counter: slot[l] holds the combined value of the latest
+// complete block of 2^l roles.  Role q arrives as a block of one; while bit l
+// of q is set, the block in slot[l] (lower roles, the receiving side) absorbs
+// it: cur = slot[l] (+) cur.  After role N-1 the occupied slots are the set
+// bits of N, and the reduce rounds combine them from the smallest block (the
+// highest roles) upward, each larger block receiving the result.  This is
+// exactly the pairing of the rounds above, with log2(N) + 1 values live
+// instead of N.  Roles are loaded in batches of kTreeBatch so that many loads
+// are in flight before the first combine.
+// ---------------------------------------------------------------------------
+struct TreeArgs {
+  RankPtrs ptrs;
+  uint64_t count;
+  uint64_t half;
+  uint64_t tiles;
+  int n;
+};
+
+constexpr int kTreeUnroll = 2;
+constexpr int kTreeBatch = 8;
+
+constexpr int ilog2_ceil(int v) { return v <= 1 ? 0 : 1 + ilog2_ceil((v + 1) / 2); }
+
+// Folds U packs (pack index idx[u], valid where live[u]) of every role of one
+// tree; LOAD(rank, u) loads rank's pack u.
+template <ar_dtype_t DT, ar_op_t OP, int NMAX, int U, class P, class Load>
+__device__ __forceinline__ void tree_fold_values(int n, int tree, const Load& load, P out[U]) {
+  constexpr int L = ilog2_ceil(NMAX) + 1;
+  P slot[L][U];
+#pragma unroll
+  for (int q0 = 0; q0 < NMAX; q0 += kTreeBatch) {
+    if (q0 >= n) break;
+    P in[kTreeBatch][U];
+#pragma unroll
+    for (int j = 0; j < kTreeBatch; ++j) {
+      const int q = q0 + j;
+      if (q < n) {
+        const int rank = tree == 0 ? q : n - 1 - q;
+#pragma unroll
+        for (int u = 0; u < U; ++u) in[j][u] = load(rank, u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTreeBatch; ++j) {
+      const int q = q0 + j;   // compile-time after unrolling
+      if (q < n) {
+        P cur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = in[j][u];
+        int l = 0;
+#pragma unroll
+        for (int bit = 0; bit < L; ++bit) {
+          if (((q >> bit) & 1) == 0) break;
+#pragma unroll
+          for (int u = 0; u < U; ++u) cur[u] = combine<DT, OP>(slot[bit][u], cur[u]);
+          l = bit + 1;
+        }
+#pragma unroll
+        for (int ll = 0; ll < L; ++ll)
+          if (ll == l) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) slot[ll][u] = cur[u];
+          }
+      }
+    }
+  }
+  bool have = false;
+#pragma unroll
+  for (int l = 0; l < L; ++l) {
+    if ((n >> l) & 1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) out[u] = have ? combine<DT, OP>(slot[l][u], out[u]) : slot[l][u];
+      have = true;
+    }
+  }
+}
+
+template <ar_dtype_t DT, ar_op_t OP, int NMAX>
+__global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
+  using T = typename Elem<DT>::T;
+  constexpr int K = 16 / sizeof(T);
+  constexpr int U = kTreeUnroll;
+  using P = Pack<T, K>;
+  using S = Pack<T, 1>;
+
+  const int n = a.n;
+  const int tree = blockIdx.y;
+  const uint64_t lo = tree == 0 ? 0 : a.half;
+  const uint64_t hi = tree == 0 ? a.half : a.count;
+  if (lo >= hi) return;
+  const Span s = make_span<K>(lo, hi);
+
+  for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+    const uint64_t tp = TileGrid<U>::first_pack(s.plo, tile);
+    if (tp >= s.phi) break;
+    const uint64_t toff = tp * 16;
+    const TileLanes<U> ln(tp, s.plo, s.phi);
+    P v[U];
+    tree_fold_values<DT, OP, NMAX, U, P>(
+        n, tree,
+        [&](int rank, int u) {
+          return ln.live[u] ? load_stream<P>(at(a.ptrs.p[rank], toff), ln.off[u]) : P{};
+        },
+        v);
+    for (int r = 0; r < n; ++r) {
+      char* dst = at(a.ptrs.p[r], toff);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ln.live[u]) store_stream<P>(dst, ln.off[u], v[u]);
+    }
+  }
+
+  if (blockIdx.x == 0 && threadIdx.x < s.scalar_count()) {
+    const uint64_t e = s.scalar_index(threadIdx.x);
+    S v[1];
+    tree_fold_values<DT, OP, NMAX, 1, S>(
+        n, tree, [&](int rank, int) { return load<S>(a.ptrs.p[rank], e); }, v);
+    for (int r = 0; r < n; ++r) store<S>(a.ptrs.p[r], e, v[0]);
+  }
+}
+
+template <ar_dtype_t DT, ar_op_t OP>
+hipError_t tree_fold_typed(const TreeArgs& a, hipStream_t stream) {
+  using T = typename Elem<DT>::T;
+  constexpr int K = 16 / sizeof(T);
+  TreeArgs b = a;
+  b.tiles = tiles_for(a.half, K, kTreeUnroll);   // tree 0's half is never the shorter one
+  const dim3 grid(grid_x(b.tiles), 2);
+  const void* fn;
+  if (a.n <= 8)
+    fn = reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 8>);
+  else if (a.n <= 16)
+    fn = reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 16>);
+  else if (a.n <= 32)
+    fn = reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 32>);
+  else
+    fn = reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, AR_MAX_RANKS>);
+  return launch(fn, grid, b, stream);
+}
+
+}  // namespace
+
+hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                            ar_op_t op, hipStream_t stream) {
+  TreeArgs a;
+  a.ptrs = ptrs;
+  a.count = count;
+  a.half = tree_split(count);
+  a.n = n;
+  a.tiles = 0;
+  AR_DISPATCH(tree_fold_typed, dtype, op, a, stream);
+}
+
+}  // namespace ar
