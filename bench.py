@@ -3,7 +3,8 @@ MI355X, through the C ABI of libar.so.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3]
                     [--workload large_grad_fp32] [--collective ring_allreduce]
-                    [--impl fused|step] [--cpu-sample 33554432 | --no-cpu-baseline]
+                    [--impl fused|step] [--flush-mall]
+                    [--no-cpu-baseline] [--no-parity] [--suite FILE.jsonl]
 
 One "step" is one collective call over the whole workload (every rank buffer
 already resident in HBM).  W untimed calls, then K timed calls bracketed by
@@ -12,22 +13,36 @@ on the stream the library launches on.  Rank 0 prints one JSON line.
 
 The collectives work in place, so step k+1 reduces step k's output: after an
 AllReduce every rank holds the sum, and each further call multiplies the
-magnitude by about N.  Normal(0, 1e-3) inputs stay finite for more than 35
-calls at N = 8 (8^35 * 1e-3 < 3.4e38), so W + K is capped there; the kernels
-have no value-dependent control flow.
+magnitude by about N.  The workloads' inputs stay finite for more than 35
+calls, so W + K is capped there; the kernels have no value-dependent control
+flow.
 
-value: algorithm bandwidth, T * itemsize / (wall time per call), as GB/s
-(1 GB = 1e9 bytes).  roofline: the fused kernel's algorithmic HBM bytes per
-launch (2 * N * T * itemsize for AllReduce: every input read once, every
-output written once) over its average event-timed duration, against the
-8 TB/s HBM peak.  cpu_baseline: the CPU checker (a literal NumPy ring
-simulation, single-threaded) timed on a bounded sample of the same inputs.
+value: algorithm bandwidth, T * itemsize / (wall time per call), in GB/s
+(1 GB = 1e9 bytes).  roofline: the dominant kernel's algorithmic HBM bytes per
+launch (2 * N * T * itemsize for a fused AllReduce: every input read once,
+every output written once) over its average event-timed duration, against the
+8 TB/s HBM peak; `traffic` is the HBM bytes per launch that rocprofv3's
+FETCH_SIZE / WRITE_SIZE counters measured for the same kernel source (from the
+committed summary under profiles/), else null.
+
+After timing, one more call runs on freshly drawn inputs and its whole output
+is compared, window by window, with the CPU checker (a literal NumPy
+simulation of the schedule, single-threaded) on the same inputs; the
+checker's time over all windows is the cpu_baseline.  With --flush-mall a
+1 GiB buffer is overwritten before every timed call (outside the events) so
+that workloads smaller than the 256 MB Infinity Cache are read from HBM;
+value then comes from the event times.
+
+--suite FILE runs every configuration of the workload table (fused and
+step-by-step implementations, ring and tree, each size of the sweep) and
+appends one JSON line per run to FILE; the headline line is printed last.
 """
 
 import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,25 +54,38 @@ METRIC = "ring AllReduce algbw GB/s and % of HBM peak, N=8 fp32 1.2 GB/rank"
 HBM_PEAK_GBPS = 8000.0
 DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
 MAX_CALLS = 35
+COLLECTIVES = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce"]
+KERNEL = {  # collective, impl -> kernel that dominates one call
+    ("ring_allreduce", "fused"): "ring_fold_kernel",
+    ("reduce_scatter", "fused"): "ring_fold_kernel",
+    ("allgather", "fused"): "fanout_kernel",
+    ("broadcast", "fused"): "fanout_kernel",
+    ("tree_allreduce", "fused"): "tree_fold_kernel",
+}
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="large_grad_fp32")
-    p.add_argument("--collective", default="ring_allreduce",
-                   choices=["ring_allreduce", "reduce_scatter", "allgather", "broadcast",
-                            "tree_allreduce"])
+    p.add_argument("--collective", default="ring_allreduce", choices=COLLECTIVES)
     p.add_argument("--impl", default="fused", choices=["fused", "step"])
-    p.add_argument("--cpu-sample", type=int, default=1 << 25,
-                   help="elements per rank of the CPU checker's sample")
-    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--root", type=int, default=0, help="broadcast root")
+    p.add_argument("--flush-mall", action="store_true")
+    p.add_argument("--cpu-window", type=int, default=1 << 24,
+                   help="elements per rank per window of the CPU checker")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the CPU checker (and with it the output comparison)")
+    p.add_argument("--no-parity", action="store_true", help="alias of --no-cpu-baseline")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                   help="also run torch copies of this many MiB (PMC scaling reference)")
+                   help="also run one device-to-device copy of this many MiB "
+                        "(the reference kernel for the PMC byte counters)")
+    p.add_argument("--suite", default=None, metavar="FILE",
+                   help="run every configuration, append JSON lines to FILE")
     p.add_argument("--jsonl", default=None, help="append the JSON line to this file too")
-    return p.parse_args()
+    return p.parse_args(argv)
 
 
 def kernel_source_hash():
@@ -72,16 +100,17 @@ def kernel_source_hash():
 
 
 def traffic_from_profile(workload, collective, impl):
-    """HBM bytes per launch from a committed PMC summary, if it was taken on the
-    current kernel source; None otherwise."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{collective}_{impl}_{workload}.json")
+    """HBM bytes per launch from the committed PMC summary of this kernel and
+    workload, if it was taken on the current kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{collective}_{impl}_{workload}.md")
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    text = open(path).read()
+    sha = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    val = re.search(r"^hbm_bytes_per_launch:\s*([0-9]+)\s*$", text, re.M)
+    if not sha or not val or sha.group(1) != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(val.group(1))
 
 
 def algorithmic_bytes(collective, n, t, isz):
@@ -95,31 +124,233 @@ def algorithmic_bytes(collective, n, t, isz):
     }[collective]
 
 
-def cpu_baseline(sample, dtype, collective, n):
+def step_bytes(collective, n, t, isz):
+    """HBM bytes of the literal schedule: 3 per element of a reduce transfer
+    (read both sides, write one), 2 per element of a copy transfer."""
+    import tree_allreduce_algorithms_amd as ar
+    sent, _ = ar.expected_bytes(collective, n, t, "bfloat16" if isz == 2 else "int32")
+    moved = sum(sent) // isz                     # elements transferred over all steps
+    # share of those elements moved by reduce (rather than copy) transfers
+    reduce_share = {"ring_allreduce": (1, 2), "tree_allreduce": (1, 2),
+                    "reduce_scatter": (1, 1)}.get(collective, (0, 1))
+    reduced = moved * reduce_share[0] // reduce_share[1]
+    return (3 * reduced + 2 * (moved - reduced)) * isz
+
+
+def run_checker(collective, pristine, got, w, root, window):
+    """Run the CPU checker over every window of the workload on the inputs in
+    `pristine`, compare with the device output `got`; returns (seconds,
+    compared elements, mismatching elements)."""
+    import numpy as np
     import oracle
+    import torch
+
+    n, t = w.nranks, w.count
+    owned = oracle.chunk_layout(n, t)
+
+    def host(x, a, b):
+        v = x[a:b]
+        if w.dtype == "bfloat16":
+            return v.view(torch.int16).cpu().numpy().view(np.uint16)
+        return v.cpu().numpy()
+
     fn = {
-        "ring_allreduce": lambda x: oracle.ring_allreduce(x, "sum", dtype),
-        "tree_allreduce": lambda x: oracle.tree_allreduce(x, "sum", dtype),
-        "reduce_scatter": lambda x: oracle.ring_reduce_scatter(x, "sum", dtype),
-        "allgather": lambda x: oracle.ring_allgather(x, dtype),
-        "broadcast": lambda x: oracle.broadcast(x, 0, dtype),
+        "ring_allreduce": lambda x, a: oracle.ring_allreduce(x, "sum", w.dtype, a, t),
+        "tree_allreduce": lambda x, a: oracle.tree_allreduce(x, "sum", w.dtype, 2, a, t),
+        "reduce_scatter": lambda x, a: oracle.ring_reduce_scatter(x, "sum", w.dtype, a, t),
+        "allgather": lambda x, a: oracle.ring_allgather(x, w.dtype, a, t),
+        "broadcast": lambda x, a: oracle.broadcast(x, root, w.dtype, a, t),
     }[collective]
+    secs, compared, bad = 0.0, 0, 0
+    for a in range(0, t, window):
+        b = min(t, a + window)
+        xin = [host(p, a, b) for p in pristine]
+        t0 = time.perf_counter()
+        want = fn(xin, a).bufs
+        secs += time.perf_counter() - t0
+        for r in range(n):
+            g = host(got[r], a, b)
+            if collective == "reduce_scatter":
+                lo, hi = max(owned[r][0], a) - a, min(owned[r][1], b) - a
+                if lo >= hi:
+                    continue
+                g, ww = g[lo:hi], want[r][lo:hi]
+            else:
+                ww = want[r]
+            compared += g.size
+            bad += int(np.count_nonzero(g != ww))
+    return secs, compared, bad
+
+
+def run_one(args):
+    import torch
+
+    import tree_allreduce_algorithms_amd as ar
+    from tree_allreduce_algorithms_amd import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    n, t, isz = w.nranks, w.count, w.itemsize
+    dev = torch.device("cuda:0")
+    ar.set_impl(args.impl)
+    print(f"[bench] workload={w.name} N={n} T={t} dtype={w.dtype} collective={args.collective} "
+          f"impl={args.impl} flush={args.flush_mall}", file=sys.stderr, flush=True)
+
+    def draw():
+        return [workloads.device_rank(w.dist, w.dtype, t, w.seed, r, dev, w.params)
+                for r in range(n)]
+
+    bufs = draw()
+    torch.cuda.synchronize()
+    call = {
+        "ring_allreduce": lambda b: ar.ring_allreduce(b),
+        "tree_allreduce": lambda b: ar.tree_allreduce(b),
+        "reduce_scatter": lambda b: ar.reduce_scatter(b),
+        "allgather": lambda b: ar.allgather(b),
+        "broadcast": lambda b: ar.broadcast(b, root=args.root),
+    }[args.collective]
+    stream = torch.cuda.current_stream(dev)
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_mall else None
+
+    for _ in range(args.warmup):
+        call(bufs)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    fn(sample)
-    secs = time.perf_counter() - t0
-    ts = len(sample[0])
-    isz = sample[0].dtype.itemsize
-    return {
-        "value": ts * isz / secs / 1e9,
+    for i in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.fill_(float(i))
+        starts[i].record(stream)
+        call(bufs)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    event_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    finite = bool(all(torch.isfinite(b[:1 << 20].float()).all().item() for b in bufs[:2]))
+    del flush_buf
+
+    launch_ms = sum(event_ms) / len(event_ms)
+    per_call_s = (launch_ms * 1e-3) if args.flush_mall else wall / args.steps
+    alg = algorithmic_bytes(args.collective, n, t, isz)
+    launches = 1 if args.impl == "fused" else ar.expected_steps(args.collective, n)
+    moved = alg if args.impl == "fused" else step_bytes(args.collective, n, t, isz)
+    achieved = moved / (launch_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(w.name, args.collective, args.impl)
+
+    result = {
+        "metric": METRIC,
+        "value": round(t * isz / per_call_s / 1e9, 3),
         "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"{collective} of N={n} rank buffers of {ts} {dtype} elements (the first "
-                  f"{ts} elements of each rank's input), literal NumPy ring simulation, "
-                  f"one thread, {secs:.2f} s",
-        "seconds": secs,
-        "host_cpus": len(os.sched_getaffinity(0)),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per_call_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_TAG[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "collective": args.collective, "impl": args.impl,
+                   "nranks": n, "count_per_rank": t, "rank_bytes": t * isz,
+                   "distribution": w.dist, "params": w.params, "seed": w.seed,
+                   "timing": "events, Infinity Cache flushed before each call"
+                   if args.flush_mall else "wall clock over the K calls"},
+        "pct_of_hbm_peak": round(100.0 * alg / per_call_s / 1e9 / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": KERNEL.get((args.collective, args.impl), "step_kernel"),
+            "algorithmic_bytes_per_launch": moved if launches == 1 else None,
+            "algorithmic_bytes_per_call": moved,
+            "launches_per_step": launches,
+            "event_ms_mean": round(launch_ms, 4),
+            "event_ms_median": round(sorted(event_ms)[len(event_ms) // 2], 4),
+            "event_ms_min": round(min(event_ms), 4),
+            "event_ms_max": round(max(event_ms), 4),
+        },
+        "outputs_finite": finite,
+        "device": torch.cuda.get_device_name(dev),
     }
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        ce0.record(stream)
+        dst.copy_(src)
+        ce1.record(stream)
+        torch.cuda.synchronize()
+        ms = ce0.elapsed_time(ce1)
+        result["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes,
+                                      "ms": round(ms, 4),
+                                      "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+        del src, dst
+
+    del bufs
+    torch.cuda.empty_cache()
+    if not (args.no_cpu_baseline or args.no_parity):
+        print("[bench] checking one call on fresh inputs against the CPU checker",
+              file=sys.stderr, flush=True)
+        pristine = draw()
+        got = [p.clone() for p in pristine]
+        call(got)
+        torch.cuda.synchronize()
+        secs, compared, bad = run_checker(args.collective, pristine, got, w, args.root,
+                                          args.cpu_window)
+        del pristine, got
+        torch.cuda.empty_cache()
+        windows = -(-t // args.cpu_window)
+        result["parity"] = {"compared_elements": compared, "mismatches": bad,
+                            "bit_exact": bad == 0}
+        result["cpu_baseline"] = {
+            "value": round(t * isz / secs / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole workload: {args.collective} of N={n} ranks x T={t} "
+                      f"{w.dtype} elements, run as {windows} windows of up to "
+                      f"{args.cpu_window} elements per rank (literal NumPy simulation of "
+                      f"the schedule, one thread), {secs:.2f} s",
+            "seconds": round(secs, 3),
+            "host_cpus": len(os.sched_getaffinity(0)),
+        }
+    return result
+
+
+SUITE = [
+    # workload, collective, impl, extra flags
+    ("large_grad_fp32", "ring_allreduce", "step", []),
+    ("large_grad_fp32", "tree_allreduce", "fused", []),
+    ("large_grad_bf16", "ring_allreduce", "fused", []),
+    ("large_grad_bf16", "ring_allreduce", "step", []),
+    ("ddp_bucket", "ring_allreduce", "fused", []),
+    ("ddp_bucket", "ring_allreduce", "fused", ["--flush-mall"]),
+    ("ddp_bucket", "ring_allreduce", "step", ["--flush-mall"]),
+    ("zero_n64", "reduce_scatter", "fused", []),
+    ("zero_n64", "allgather", "fused", []),
+    ("zero_n64", "broadcast", "fused", []),
+    ("zero_n64", "reduce_scatter", "step", []),
+    ("zero_n64", "allgather", "step", []),
+    ("zero_n64", "broadcast", "step", []),
+    ("small_int32", "ring_allreduce", "fused", ["--steps", "30"]),
+    ("small_int32", "reduce_scatter", "fused", ["--steps", "30"]),
+    ("small_int32", "allgather", "fused", ["--steps", "30"]),
+    ("small_int32", "ring_allreduce", "step", ["--steps", "30"]),
+] + [
+    (f"sweep_{t}", coll, impl, ["--steps", "30"] + (["--flush-mall"] if t >= 262_144 else []))
+    for t in (256, 262_144, 4_194_304, 67_108_864)
+    for coll in ("ring_allreduce", "tree_allreduce")
+    for impl in ("fused", "step")
+]
 
 
 def main():
@@ -135,137 +366,41 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import tree_allreduce_algorithms_amd as ar
-    from tree_allreduce_algorithms_amd import binding, workloads
+    from tree_allreduce_algorithms_amd import binding
 
     if not os.path.exists(binding.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
     ar.lib()
-    ar.set_impl(args.impl)
+    torch.cuda.set_device(0)
 
-    w = workloads.WORKLOADS[args.workload]
-    n, t, isz = w.nranks, w.count, w.itemsize
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    print(f"[bench] workload={w.name} N={n} T={t} dtype={w.dtype} collective={args.collective} "
-          f"impl={args.impl}", file=sys.stderr, flush=True)
-    bufs = [workloads.device_rank(w.dist, w.dtype, t, w.seed, r, dev, w.params) for r in range(n)]
-    torch.cuda.synchronize()
+    failed = False
+    if args.suite:
+        base = ["--warmup", "3"]
+        for wname, coll, impl, extra in SUITE:
+            sub = parse(base + ["--workload", wname, "--collective", coll, "--impl", impl] + extra)
+            res = run_one(sub)
+            failed |= not res.get("parity", {}).get("bit_exact", True)
+            with open(args.suite, "a") as f:
+                f.write(json.dumps(res) + "\n")
+            print(f"[suite] {wname} {coll} {impl} {' '.join(extra)}: "
+                  f"{res['roofline']['event_ms_mean']} ms/call, "
+                  f"{res['roofline']['achieved']} GB/s, parity "
+                  f"{res.get('parity', {}).get('bit_exact')}", file=sys.stderr, flush=True)
 
-    sample = None
-    if not args.no_cpu_baseline:
-        ts = min(args.cpu_sample, t)
-        if w.dtype == "bfloat16":
-            sample = [b[:ts].view(torch.int16).cpu().numpy().view(np.uint16) for b in bufs]
-        else:
-            sample = [b[:ts].cpu().numpy() for b in bufs]
-
-    call = {
-        "ring_allreduce": lambda: ar.ring_allreduce(bufs),
-        "tree_allreduce": lambda: ar.tree_allreduce(bufs),
-        "reduce_scatter": lambda: ar.reduce_scatter(bufs),
-        "allgather": lambda: ar.allgather(bufs),
-        "broadcast": lambda: ar.broadcast(bufs, root=0),
-    }[args.collective]
-    stream = torch.cuda.current_stream(dev)
-
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    print(f"[bench] warmup done, timing {args.steps} calls", file=sys.stderr, flush=True)
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    event_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    finite = bool(all(torch.isfinite(b[:1 << 20].float()).all().item() for b in bufs[:2]))
-
-    ms_per_step = wall / args.steps * 1e3
-    value = t * isz / (wall / args.steps) / 1e9
-    launch_ms = sum(event_ms) / len(event_ms)
-    alg = algorithmic_bytes(args.collective, n, t, isz)
-    achieved = alg / (launch_ms * 1e-3) / 1e9
-    launches = 1 if args.impl == "fused" else ar.expected_steps(args.collective, n)
-    traffic = traffic_from_profile(w.name, args.collective, args.impl)
-
-    result = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": DTYPE_TAG[w.dtype],
-        "device": torch.cuda.get_device_name(dev),
-        "data": "synthetic",
-        "config": {"workload": w.name, "collective": args.collective, "impl": args.impl,
-                   "nranks": n, "count_per_rank": t, "rank_bytes": t * isz,
-                   "distribution": w.dist, "params": w.params, "seed": w.seed},
-        "pct_of_hbm_peak": round(100.0 * alg / (wall / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": alg if launches == 1 else None,
-            "algorithmic_bytes_per_call": alg,
-            "launches_per_step": launches,
-            "event_ms_mean": round(launch_ms, 4),
-            "event_ms_min": round(min(event_ms), 4),
-            "event_ms_max": round(max(event_ms), 4),
-        },
-        "outputs_finite": finite,
-    }
-
-    if args.copy_calibration:
-        nbytes = args.copy_calibration << 20
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        ce0.record(stream)
-        reps = 5
-        for _ in range(reps):
-            dst.copy_(src)
-        ce1.record(stream)
-        torch.cuda.synchronize()
-        ms = ce0.elapsed_time(ce1) / reps
-        result["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes,
-                                      "ms": round(ms, 4),
-                                      "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
-        del src, dst
-
-    del bufs
-    torch.cuda.empty_cache()
-    if sample is not None:
-        print(f"[bench] timing the CPU checker on {len(sample[0])} elements per rank",
-              file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(sample, w.dtype, args.collective, n)
-
+    result = run_one(args)
+    failed |= not result.get("parity", {}).get("bit_exact", True)
     line = json.dumps(result)
     print(line, flush=True)
-    if args.jsonl:
-        with open(args.jsonl, "a") as f:
+    for path in filter(None, (args.jsonl, args.suite)):
+        with open(path, "a") as f:
             f.write(line + "\n")
+    if failed:
+        print("[bench] the device output differs from the CPU checker", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

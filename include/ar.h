@@ -37,8 +37,8 @@
  *           AR_FLOAT32  one IEEE binary32 operation, round to nearest even,
  *                       subnormals kept, never fused or reassociated;
  *           AR_BFLOAT16 widen both to binary32, apply the op, round back to
- *                       bfloat16 to nearest even after EVERY hop (NaN ->
- *                       quiet NaN, sign and top payload kept);
+ *                       bfloat16 to nearest even after EVERY hop (a NaN
+ *                       stays a NaN; its payload bits are unspecified);
  *           MAX / MIN   keep the local value unless the incoming one compares
  *                       strictly greater / smaller.
  *         The ring calls reproduce the ring's order per element exactly

@@ -75,7 +75,7 @@ hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t
   a.n = n;
   a.root = from_root ? root : -1;
   const int pack = static_cast<int>(16 / itemsize(dtype));
-  const int u = pick_unroll(n);
+  const int u = pick_unroll(UnrollFor::kFanout, n);
   a.tiles = tiles_for(a.chunk, pack, u);
   const dim3 grid(grid_x(a.tiles), n);
   const void* fn = itemsize(dtype) == 2 ? fanout_fn<uint16_t>(u) : fanout_fn<uint32_t>(u);

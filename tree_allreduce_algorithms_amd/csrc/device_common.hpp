@@ -257,20 +257,23 @@ inline uint64_t tiles_for(uint64_t max_elems, int pack, int unroll) {
   return (packs + per_tile - 1) / per_tile + 1;
 }
 
-// Packs per lane per tile for a kernel over N ranks.  A tile moves about
-// (N reads + N writes) * U * 4 KiB per block, so the unroll shrinks as N grows
-// to keep blocks short enough that the last ones do not leave most of the chip
-// idle.  AR_TUNE_UNROLL (1, 2 or 4), read at the first launch, overrides the
-// choice for measurements; it changes nothing but the pack grouping, never
-// any element's arithmetic.
-inline int pick_unroll(int n) {
+// Packs per lane per tile.  Measured on gfx950 with interleaved repeats over
+// 8 x 1.2 GB and 64 x 64 MB rank buffers: the ring fold is best or tied at one
+// pack per lane for every N (each lane already keeps N loads in flight); the
+// fan-out copy is best at four packs for N <= 8 and at two above.  AR_TUNE_UNROLL (1, 2 or 4), read at the first
+// launch, overrides both for measurements; it changes nothing but the pack
+// grouping, never any element's arithmetic.
+enum class UnrollFor { kFold, kFanout };
+
+inline int pick_unroll(UnrollFor kind, int n) {
   static const int forced = [] {
     const char* v = std::getenv("AR_TUNE_UNROLL");
     const int u = v != nullptr ? std::atoi(v) : 0;
     return (u == 1 || u == 2 || u == 4) ? u : 0;
   }();
   if (forced != 0) return forced;
-  return n <= 8 ? 4 : (n <= 16 ? 2 : 1);
+  if (kind == UnrollFor::kFold) return 1;
+  return n <= 8 ? 4 : 2;
 }
 
 inline uint32_t grid_x(uint64_t tiles) {

@@ -104,7 +104,7 @@ const void* ring_fold_fn(int u) {
 template <ar_dtype_t DT, ar_op_t OP>
 hipError_t ring_fold_typed(FoldArgs a, bool all, hipStream_t stream) {
   constexpr int K = 16 / sizeof(typename Elem<DT>::T);
-  const int u = pick_unroll(a.n);
+  const int u = pick_unroll(UnrollFor::kFold, a.n);
   a.tiles = tiles_for(a.chunk, K, u);
   const dim3 grid(grid_x(a.tiles), a.n);
   return launch(all ? ring_fold_fn<DT, OP, true>(u) : ring_fold_fn<DT, OP, false>(u), grid, a,
