@@ -19,7 +19,10 @@
  * --------------------------------------------
  * bufs    HOST array of `nranks` DEVICE pointers; bufs[r] is rank r's buffer
  *         of `count` contiguous elements of `dtype`.  Every buffer must be
- *         aligned to the element size, and no two buffers may overlap.  The
+ *         aligned to the element size, and no two buffers may overlap.  When
+ *         every buffer is 16-byte aligned the kernels move 16-byte packs;
+ *         otherwise they move one element at a time, with the same
+ *         arithmetic in the same order (identical results, lower speed).  The
  *         caller allocates and owns every buffer; the library never
  *         allocates user memory and keeps no pointer after returning (the
  *         pointers travel inside kernel arguments).

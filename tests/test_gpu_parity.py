@@ -252,15 +252,52 @@ def test_non_default_stream():
         assert_same(to_host(bufs[r], "float32"), want[r], "float32", f"rank {r}")
 
 
-def test_unaligned_buffers_are_rejected_untouched():
-    base = torch.arange(4 * 1001 + 4, dtype=torch.float32, device=DEV)
-    views = [base[1 + r * 1001: 1 + (r + 1) * 1001] for r in range(4)]   # 4-byte, not 16-byte
-    keep = base.clone()
-    status = binding.raw_call("ring_allreduce", [v.data_ptr() for v in views], 1001, "float32",
-                              op="sum", stream=0)
-    torch.cuda.synchronize()
-    assert status == binding.UNSUPPORTED
-    assert torch.equal(base, keep)
+def _element_aligned_views(n, t, dtype, offsets):
+    """Rank buffers as views into one allocation, rank r starting `offsets[r]`
+    elements past a 256-byte boundary (so 4- or 2-byte aligned, not 16)."""
+    stride = t + 64
+    base = torch.zeros(n * stride + 64, dtype=TORCH_DT[dtype], device=DEV)
+    return base, [base[r * stride + offsets[r]: r * stride + offsets[r] + t] for r in range(n)]
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "int32"])
+@pytest.mark.parametrize("layout", ["all_offset", "mixed"])
+def test_element_aligned_buffers_match_oracle(dtype, layout):
+    """Buffers aligned only to the element size take the element-at-a-time
+    path; its results must equal the oracle bit for bit, for every collective
+    and both implementations, without touching memory outside the views."""
+    n, t = 5, 10_007
+    offsets = [1] * n if layout == "all_offset" else [r % 3 for r in range(n)]
+    dist = "int_uniform" if dtype == "int32" else "normal"
+    x = workloads.host_inputs(n, t, dtype, dist, 51, _params(dist, n))
+    owned = oracle.chunk_layout(n, t)
+    for coll in sorted(CALLS):
+        want = CALLS[coll][1](x, "sum", dtype, 1).bufs
+        for impl in IMPLS:
+            announce(f"element-aligned {coll} impl={impl} dtype={dtype} layout={layout}")
+            ar.set_impl(impl)
+            base, views = _element_aligned_views(n, t, dtype, offsets)
+            src = to_dev(x, dtype)
+            for v, s_ in zip(views, src):
+                v.copy_(s_)
+            outside = base.clone()
+            for v in views:
+                outside[v.storage_offset(): v.storage_offset() + t] = 0
+            CALLS[coll][0](views, "sum", 1)
+            torch.cuda.synchronize()
+            for r in range(n):
+                got = to_host(views[r], dtype)
+                if coll == "reduce_scatter":
+                    lo, hi = owned[r]
+                    assert_same(got[lo:hi], want[r][lo:hi], dtype, f"{coll}/{impl} rank {r}")
+                else:
+                    assert_same(got, want[r], dtype, f"{coll}/{impl} rank {r}")
+            after = base.clone()
+            for v in views:
+                after[v.storage_offset(): v.storage_offset() + t] = 0
+            assert torch.equal(after.view(torch.int16) if dtype == "bfloat16" else after,
+                               outside.view(torch.int16) if dtype == "bfloat16" else outside)
+    ar.set_impl("fused")
 
 
 # --- full-size workloads: sampled windows --------------------------------------
@@ -401,3 +438,64 @@ def test_rank_buffers_beyond_4_gib():
     assert _ranks_identical(bufs)
     del bufs
     torch.cuda.empty_cache()
+
+
+# --- bfloat16 edge values -------------------------------------------------------
+
+def test_bfloat16_subnormals_ties_and_overflow():
+    """bfloat16 inputs chosen so that per-hop float32 sums land on exact ties,
+    in the subnormal range, and beyond the largest finite bfloat16: the
+    device rounding (nearest even after every hop) must equal the oracle's."""
+    rng = np.random.default_rng(77)
+    n, t = 6, 8_191
+    pools = [
+        np.array([0x3F80, 0x3B80, 0x3F81, 0xBB80, 0x3C00, 0xBF80], dtype=np.uint16),  # ties
+        rng.integers(0x0001, 0x0080, size=64, dtype=np.uint16),                          # subnormal
+        rng.integers(0x8001, 0x8080, size=64, dtype=np.uint16),
+        np.array([0x7F7F, 0x7F7E, 0xFF7F, 0x7F00], dtype=np.uint16),                     # near max
+    ]
+    pool = np.concatenate(pools)
+    x = [pool[rng.integers(0, pool.size, size=t)] for _ in range(n)]
+    for coll in ("ring_allreduce", "tree_allreduce", "reduce_scatter"):
+        for op in ("sum", "prod"):
+            compare_collective(coll, x, "bfloat16", op, 0)
+
+
+# --- HIP graph capture ------------------------------------------------------------
+
+@pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce", "reduce_scatter",
+                                  "allgather", "broadcast"])
+def test_graph_capture_replays_match_eager(coll, impl):
+    """A collective captured into a HIP graph (kernel launches only; the
+    library records no memset) replays correctly several times in a row, with
+    eager work and synchronisations between the replays."""
+    n, t = 8, 100_003
+    x = workloads.host_inputs(n, t, "float32", "normal", 61, {"std": 1.0})
+    want = CALLS[coll][1](x, "sum", "float32", 2).bufs
+    owned = oracle.chunk_layout(n, t)
+    ar.set_impl(impl)
+    bufs = to_dev(x, "float32")
+    pristine = [b.clone() for b in bufs]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        CALLS[coll][0](bufs, "sum", 2)
+    for replay in range(3):
+        announce(f"graph replay {replay} {coll} impl={impl}")
+        for b, p in zip(bufs, pristine):
+            b.copy_(p)
+        scratch = torch.randn(1 << 16, device=DEV).sum()   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        for r in range(n):
+            got = to_host(bufs[r], "float32")
+            if coll == "reduce_scatter":
+                lo, hi = owned[r]
+                assert_same(got[lo:hi], want[r][lo:hi], "float32", f"replay {replay} rank {r}")
+            else:
+                assert_same(got, want[r], "float32", f"replay {replay} rank {r}")
+    del graph
+    ar.set_impl("fused")

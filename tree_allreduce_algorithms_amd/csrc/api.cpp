@@ -64,33 +64,33 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const ar_impl_t impl = static_cast<ar_impl_t>(g_impl.load());
 
-  // The kernels move 16-byte packs at element indices that are multiples of
-  // the pack width, which needs every buffer 16-byte aligned.  Buffers that
-  // are only element-aligned are not supported by this build.
-  if (!aligned16) return AR_ERROR_UNSUPPORTED;
+  // 16-byte packs need every buffer 16-byte aligned (pack p of every rank
+  // then covers the same elements); otherwise the kernels move one element
+  // at a time, with the same arithmetic in the same order.
+  const bool vec = aligned16;
 
   hipError_t err = hipSuccess;
   if (impl == AR_IMPL_STEP) {
     for (const ar::Step& s : sched) {
-      err = ar::launch_step(ptrs, s, dtype, aop, stream);
+      err = ar::launch_step(ptrs, s, dtype, aop, vec, stream);
       if (err != hipSuccess) break;
     }
   } else {
     switch (coll) {
       case AR_RING_ALLREDUCE:
-        err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, true, stream);
+        err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, true, vec, stream);
         break;
       case AR_REDUCE_SCATTER:
-        err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, stream);
+        err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, vec, stream);
         break;
       case AR_ALLGATHER:
-        err = ar::launch_fanout(ptrs, n, count, dtype, false, 0, stream);
+        err = ar::launch_fanout(ptrs, n, count, dtype, false, 0, vec, stream);
         break;
       case AR_BROADCAST:
-        err = ar::launch_fanout(ptrs, n, count, dtype, true, root, stream);
+        err = ar::launch_fanout(ptrs, n, count, dtype, true, root, vec, stream);
         break;
       case AR_TREE_ALLREDUCE:
-        err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, stream);
+        err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, vec, stream);
         break;
     }
   }

@@ -16,10 +16,10 @@ struct FanoutArgs {
   int root;   // < 0: AllGather
 };
 
-template <class T, int U>
+template <class T, int U, bool VEC>
 __global__ __launch_bounds__(kBlock) void fanout_kernel(FanoutArgs a) {
-  constexpr int K = 16 / sizeof(T);
-  using P = Pack<T, K>;
+  constexpr int K = PackOf<T, VEC>::K;
+  using P = typename PackOf<T, VEC>::P;
   using S = Pack<T, 1>;
 
   const int n = a.n;
@@ -33,8 +33,8 @@ __global__ __launch_bounds__(kBlock) void fanout_kernel(FanoutArgs a) {
   for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
     const uint64_t tp = TileGrid<U>::first_pack(s.plo, tile);
     if (tp >= s.phi) break;
-    const uint64_t toff = tp * 16;
-    const TileLanes<U> ln(tp, s.plo, s.phi);
+    const uint64_t toff = tp * sizeof(P);
+    const TileLanes<U, sizeof(P)> ln(tp, s.plo, s.phi);
     const char* sp = at(a.ptrs.p[src], toff);
     P v[U];
 #pragma unroll
@@ -58,27 +58,28 @@ __global__ __launch_bounds__(kBlock) void fanout_kernel(FanoutArgs a) {
 }
 
 template <class T>
-const void* fanout_fn(int u) {
-  if (u == 4) return reinterpret_cast<const void*>(&fanout_kernel<T, 4>);
-  if (u == 2) return reinterpret_cast<const void*>(&fanout_kernel<T, 2>);
-  return reinterpret_cast<const void*>(&fanout_kernel<T, 1>);
+const void* fanout_fn(int u, bool vec) {
+  if (!vec) return reinterpret_cast<const void*>(&fanout_kernel<T, 1, false>);
+  if (u == 4) return reinterpret_cast<const void*>(&fanout_kernel<T, 4, true>);
+  if (u == 2) return reinterpret_cast<const void*>(&fanout_kernel<T, 2, true>);
+  return reinterpret_cast<const void*>(&fanout_kernel<T, 1, true>);
 }
 
 }  // namespace
 
 hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                         bool from_root, int root, hipStream_t stream) {
+                         bool from_root, int root, bool vec, hipStream_t stream) {
   FanoutArgs a;
   a.ptrs = ptrs;
   a.count = count;
   a.chunk = chunk_size(n, count);
   a.n = n;
   a.root = from_root ? root : -1;
-  const int pack = static_cast<int>(16 / itemsize(dtype));
-  const int u = pick_unroll(UnrollFor::kFanout, n);
+  const int pack = vec ? static_cast<int>(16 / itemsize(dtype)) : 1;
+  const int u = vec ? pick_unroll(UnrollFor::kFanout, n) : 1;
   a.tiles = tiles_for(a.chunk, pack, u);
   const dim3 grid(grid_x(a.tiles), n);
-  const void* fn = itemsize(dtype) == 2 ? fanout_fn<uint16_t>(u) : fanout_fn<uint32_t>(u);
+  const void* fn = itemsize(dtype) == 2 ? fanout_fn<uint16_t>(u, vec) : fanout_fn<uint32_t>(u, vec);
   return launch(fn, grid, a, stream);
 }
 

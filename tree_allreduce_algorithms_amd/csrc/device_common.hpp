@@ -171,16 +171,33 @@ __device__ __forceinline__ char* at(void* p, uint64_t byte_off) {
   return static_cast<char*>(p) + byte_off;
 }
 
+// 16-byte packs go through the streaming hint; single elements (the path for
+// buffers aligned only to the element size) are plain accesses.
 template <class P> __device__ __forceinline__ P load_stream(const char* base, uint32_t off) {
-  static_assert(sizeof(P) == 16, "streaming accesses move 16-byte packs");
-  const Raw16 v = __builtin_nontemporal_load(reinterpret_cast<const Raw16*>(base + off));
-  return __builtin_bit_cast(P, v);
+  if constexpr (sizeof(P) == 16) {
+    const Raw16 v = __builtin_nontemporal_load(reinterpret_cast<const Raw16*>(base + off));
+    return __builtin_bit_cast(P, v);
+  } else {
+    return *reinterpret_cast<const P*>(base + off);
+  }
 }
 template <class P>
 __device__ __forceinline__ void store_stream(char* base, uint32_t off, const P& v) {
-  static_assert(sizeof(P) == 16, "streaming accesses move 16-byte packs");
-  __builtin_nontemporal_store(__builtin_bit_cast(Raw16, v), reinterpret_cast<Raw16*>(base + off));
+  if constexpr (sizeof(P) == 16) {
+    __builtin_nontemporal_store(__builtin_bit_cast(Raw16, v), reinterpret_cast<Raw16*>(base + off));
+  } else {
+    *reinterpret_cast<P*>(base + off) = v;
+  }
 }
+
+// Element type T moved either as 16-byte packs (VEC: every rank buffer is
+// 16-byte aligned) or one element at a time (buffers aligned only to the
+// element size).  Both paths apply the same per-element arithmetic in the
+// same order, so their results are identical.
+template <class T, bool VEC> struct PackOf {
+  static constexpr int K = VEC ? static_cast<int>(16 / sizeof(T)) : 1;
+  using P = Pack<T, K>;
+};
 
 // Elements [lo, hi) of a segment split into an element-wise head, whole
 // K-element packs [plo, phi) and an element-wise tail.
@@ -226,8 +243,9 @@ template <int U> struct TileGrid {
 };
 
 // Per-tile lane setup: live[u] says whether the lane's pack u lies inside the
-// segment's packs [plo, phi), off[u] is its byte offset inside the tile.
-template <int U> struct TileLanes {
+// segment's packs [plo, phi), off[u] is its byte offset inside the tile (PB
+// bytes per pack).
+template <int U, int PB> struct TileLanes {
   bool live[U];
   uint32_t off[U];
   __device__ TileLanes(uint64_t tile_pack, uint64_t plo, uint64_t phi) {
@@ -236,7 +254,7 @@ template <int U> struct TileLanes {
       const uint32_t lane_pack = threadIdx.x + static_cast<uint32_t>(u * kBlock);
       const uint64_t p = tile_pack + lane_pack;
       live[u] = p >= plo && p < phi;
-      off[u] = lane_pack * 16u;
+      off[u] = lane_pack * static_cast<uint32_t>(PB);
     }
   }
 };

@@ -1,5 +1,8 @@
 // Kernel launchers for the collectives (gfx950).  Every launcher enqueues on
 // `stream` and returns the hipError_t of the launch; none synchronises.
+// `vec` selects 16-byte packs (every rank buffer 16-byte aligned) or the
+// element-at-a-time path (buffers aligned only to the element size); the two
+// give identical results.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,20 +23,20 @@ struct RankPtrs {
 // the result into every rank (all_ranks, AllReduce) or into rank c only
 // (ReduceScatter).
 hipError_t launch_ring_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                            ar_op_t op, bool all_ranks, hipStream_t stream);
+                            ar_op_t op, bool all_ranks, bool vec, hipStream_t stream);
 
 // Fused fan-out copy: for every element i of chunk c, copy from rank c
 // (allgather) or from `root` (broadcast) into every other rank.
 hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                         bool from_root, int root, hipStream_t stream);
+                         bool from_root, int root, bool vec, hipStream_t stream);
 
 // Fused double binomial tree: per element, the pairwise fold of the tree that
 // owns it, stored into every rank.
 hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                            ar_op_t op, hipStream_t stream);
+                            ar_op_t op, bool vec, hipStream_t stream);
 
 // One schedule step: all of its transfers in one launch.
 hipError_t launch_step(const RankPtrs& ptrs, const Step& step, ar_dtype_t dtype, ar_op_t op,
-                       hipStream_t stream);
+                       bool vec, hipStream_t stream);
 
 }  // namespace ar

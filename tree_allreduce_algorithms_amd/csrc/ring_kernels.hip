@@ -22,13 +22,14 @@ struct FoldArgs {
 };
 
 // U: packs per lane per tile.  ALL: store into every rank (AllReduce) or only
-// into the chunk's owner (ReduceScatter).
-template <ar_dtype_t DT, ar_op_t OP, bool ALL, int U>
+// into the chunk's owner (ReduceScatter).  VEC: 16-byte packs, else one
+// element per pack.
+template <ar_dtype_t DT, ar_op_t OP, bool ALL, int U, bool VEC>
 __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
   using T = typename Elem<DT>::T;
-  constexpr int K = 16 / sizeof(T);
+  constexpr int K = PackOf<T, VEC>::K;
   constexpr int B = kFoldBatch;
-  using P = Pack<T, K>;
+  using P = typename PackOf<T, VEC>::P;
   using S = Pack<T, 1>;
 
   const int n = a.n;
@@ -42,8 +43,8 @@ __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
   for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
     const uint64_t tp = TileGrid<U>::first_pack(s.plo, tile);
     if (tp >= s.phi) break;
-    const uint64_t toff = tp * 16;
-    const TileLanes<U> ln(tp, s.plo, s.phi);
+    const uint64_t toff = tp * sizeof(P);
+    const TileLanes<U, sizeof(P)> ln(tp, s.plo, s.phi);
 
     P acc[U];
     for (int k0 = 0; k0 < n; k0 += B) {
@@ -95,33 +96,34 @@ __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
 }
 
 template <ar_dtype_t DT, ar_op_t OP, bool ALL>
-const void* ring_fold_fn(int u) {
-  if (u == 4) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 4>);
-  if (u == 2) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 2>);
-  return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 1>);
+const void* ring_fold_fn(int u, bool vec) {
+  if (!vec) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 1, false>);
+  if (u == 4) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 4, true>);
+  if (u == 2) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 2, true>);
+  return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 1, true>);
 }
 
 template <ar_dtype_t DT, ar_op_t OP>
-hipError_t ring_fold_typed(FoldArgs a, bool all, hipStream_t stream) {
+hipError_t ring_fold_typed(FoldArgs a, bool all, bool vec, hipStream_t stream) {
   constexpr int K = 16 / sizeof(typename Elem<DT>::T);
-  const int u = pick_unroll(UnrollFor::kFold, a.n);
-  a.tiles = tiles_for(a.chunk, K, u);
+  const int u = vec ? pick_unroll(UnrollFor::kFold, a.n) : 1;
+  a.tiles = tiles_for(a.chunk, vec ? K : 1, u);
   const dim3 grid(grid_x(a.tiles), a.n);
-  return launch(all ? ring_fold_fn<DT, OP, true>(u) : ring_fold_fn<DT, OP, false>(u), grid, a,
-                stream);
+  return launch(all ? ring_fold_fn<DT, OP, true>(u, vec) : ring_fold_fn<DT, OP, false>(u, vec),
+                grid, a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_ring_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                            ar_op_t op, bool all_ranks, hipStream_t stream) {
+                            ar_op_t op, bool all_ranks, bool vec, hipStream_t stream) {
   FoldArgs a;
   a.ptrs = ptrs;
   a.count = count;
   a.chunk = chunk_size(n, count);
   a.n = n;
   a.tiles = 0;
-  AR_DISPATCH(ring_fold_typed, dtype, op, a, all_ranks, stream);
+  AR_DISPATCH(ring_fold_typed, dtype, op, a, all_ranks, vec, stream);
 }
 
 }  // namespace ar

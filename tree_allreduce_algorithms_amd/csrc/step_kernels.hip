@@ -23,12 +23,12 @@ struct StepArgs {
   uint64_t tiles;
 };
 
-template <ar_dtype_t DT, ar_op_t OP, bool REDUCE>
+template <ar_dtype_t DT, ar_op_t OP, bool REDUCE, bool VEC>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
   using T = typename Elem<DT>::T;
-  constexpr int K = 16 / sizeof(T);
-  constexpr int U = kStepUnroll;
-  using P = Pack<T, K>;
+  constexpr int K = PackOf<T, VEC>::K;
+  constexpr int U = VEC ? kStepUnroll : 1;
+  using P = typename PackOf<T, VEC>::P;
   using S = Pack<T, 1>;
 
   const int j = blockIdx.y;
@@ -42,8 +42,8 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
   for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
     const uint64_t tp = TileGrid<U>::first_pack(s.plo, tile);
     if (tp >= s.phi) break;
-    const uint64_t toff = tp * 16;
-    const TileLanes<U> ln(tp, s.plo, s.phi);
+    const uint64_t toff = tp * sizeof(P);
+    const TileLanes<U, sizeof(P)> ln(tp, s.plo, s.phi);
     const char* sp = at(src, toff);
     char* dp = at(dst, toff);
     P in[U];
@@ -69,16 +69,22 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
 }
 
 template <ar_dtype_t DT, ar_op_t OP>
-hipError_t step_typed(const StepArgs& a, int nxfers, bool reduce, hipStream_t stream) {
+hipError_t step_typed(const StepArgs& a, int nxfers, bool reduce, bool vec, hipStream_t stream) {
   const dim3 grid(grid_x(a.tiles), nxfers);
-  if (reduce) return launch(reinterpret_cast<const void*>(&step_kernel<DT, OP, true>), grid, a, stream);
-  return launch(reinterpret_cast<const void*>(&step_kernel<DT, AR_SUM, false>), grid, a, stream);
+  const void* fn;
+  if (reduce)
+    fn = vec ? reinterpret_cast<const void*>(&step_kernel<DT, OP, true, true>)
+             : reinterpret_cast<const void*>(&step_kernel<DT, OP, true, false>);
+  else
+    fn = vec ? reinterpret_cast<const void*>(&step_kernel<DT, AR_SUM, false, true>)
+             : reinterpret_cast<const void*>(&step_kernel<DT, AR_SUM, false, false>);
+  return launch(fn, grid, a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_step(const RankPtrs& ptrs, const Step& step, ar_dtype_t dtype, ar_op_t op,
-                       hipStream_t stream) {
+                       bool vec, hipStream_t stream) {
   const int nx = static_cast<int>(step.xfers.size());
   if (nx == 0) return hipSuccess;
   if (nx > AR_MAX_RANKS) return hipErrorInvalidValue;
@@ -93,8 +99,9 @@ hipError_t launch_step(const RankPtrs& ptrs, const Step& step, ar_dtype_t dtype,
     longest = std::max(longest, x.hi - x.lo);
   }
   if (longest == 0) return hipSuccess;
-  a.tiles = tiles_for(longest, static_cast<int>(16 / itemsize(dtype)), kStepUnroll);
-  AR_DISPATCH(step_typed, dtype, op, a, nx, step.reduce, stream);
+  a.tiles = vec ? tiles_for(longest, static_cast<int>(16 / itemsize(dtype)), kStepUnroll)
+              : tiles_for(longest, 1, 1);
+  AR_DISPATCH(step_typed, dtype, op, a, nx, step.reduce, vec, stream);
 }
 
 }  // namespace ar

@@ -89,12 +89,12 @@ __device__ __forceinline__ void tree_fold_values(int n, int tree, const Load& lo
   }
 }
 
-template <ar_dtype_t DT, ar_op_t OP, int NMAX>
+template <ar_dtype_t DT, ar_op_t OP, int NMAX, bool VEC>
 __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
   using T = typename Elem<DT>::T;
-  constexpr int K = 16 / sizeof(T);
+  constexpr int K = PackOf<T, VEC>::K;
   constexpr int U = kTreeUnroll;
-  using P = Pack<T, K>;
+  using P = typename PackOf<T, VEC>::P;
   using S = Pack<T, 1>;
 
   const int n = a.n;
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
   for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
     const uint64_t tp = TileGrid<U>::first_pack(s.plo, tile);
     if (tp >= s.phi) break;
-    const uint64_t toff = tp * 16;
-    const TileLanes<U> ln(tp, s.plo, s.phi);
+    const uint64_t toff = tp * sizeof(P);
+    const TileLanes<U, sizeof(P)> ln(tp, s.plo, s.phi);
     P v[U];
     tree_fold_values<DT, OP, NMAX, U, P>(
         n, tree,
@@ -133,36 +133,35 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
   }
 }
 
+template <ar_dtype_t DT, ar_op_t OP, bool VEC>
+const void* tree_fold_fn(int n) {
+  if (n <= 8) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 8, VEC>);
+  if (n <= 16) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 16, VEC>);
+  if (n <= 32) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 32, VEC>);
+  return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, AR_MAX_RANKS, VEC>);
+}
+
 template <ar_dtype_t DT, ar_op_t OP>
-hipError_t tree_fold_typed(const TreeArgs& a, hipStream_t stream) {
-  using T = typename Elem<DT>::T;
-  constexpr int K = 16 / sizeof(T);
+hipError_t tree_fold_typed(const TreeArgs& a, bool vec, hipStream_t stream) {
+  constexpr int K = 16 / sizeof(typename Elem<DT>::T);
   TreeArgs b = a;
-  b.tiles = tiles_for(a.half, K, kTreeUnroll);   // tree 0's half is never the shorter one
+  b.tiles = tiles_for(a.half, vec ? K : 1, kTreeUnroll);   // tree 0's half is never the shorter
   const dim3 grid(grid_x(b.tiles), 2);
-  const void* fn;
-  if (a.n <= 8)
-    fn = reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 8>);
-  else if (a.n <= 16)
-    fn = reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 16>);
-  else if (a.n <= 32)
-    fn = reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 32>);
-  else
-    fn = reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, AR_MAX_RANKS>);
-  return launch(fn, grid, b, stream);
+  return launch(vec ? tree_fold_fn<DT, OP, true>(a.n) : tree_fold_fn<DT, OP, false>(a.n), grid, b,
+                stream);
 }
 
 }  // namespace
 
 hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                            ar_op_t op, hipStream_t stream) {
+                            ar_op_t op, bool vec, hipStream_t stream) {
   TreeArgs a;
   a.ptrs = ptrs;
   a.count = count;
   a.half = tree_split(count);
   a.n = n;
   a.tiles = 0;
-  AR_DISPATCH(tree_fold_typed, dtype, op, a, stream);
+  AR_DISPATCH(tree_fold_typed, dtype, op, a, vec, stream);
 }
 
 }  // namespace ar
