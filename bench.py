@@ -39,6 +39,7 @@ appends one JSON line per run to FILE; the headline line is printed last.
 """
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -54,7 +55,8 @@ METRIC = "ring AllReduce algbw GB/s and % of HBM peak, N=8 fp32 1.2 GB/rank"
 HBM_PEAK_GBPS = 8000.0
 DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
 MAX_CALLS = 35
-COLLECTIVES = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce"]
+COLLECTIVES = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce",
+               "allreduce"]
 KERNEL = {  # collective, impl -> kernel that dominates one call
     ("ring_allreduce", "fused"): "ring_fold_kernel",
     ("reduce_scatter", "fused"): "ring_fold_kernel",
@@ -201,7 +203,11 @@ def run_one(args):
 
     bufs = draw()
     torch.cuda.synchronize()
+    # "allreduce" runs the ring or the tree by the library's cost model
+    ran = (ar.allreduce_choice(n, t, w.dtype) if args.collective == "allreduce"
+           else args.collective)
     call = {
+        "allreduce": lambda b: ar.allreduce(b),
         "ring_allreduce": lambda b: ar.ring_allreduce(b),
         "tree_allreduce": lambda b: ar.tree_allreduce(b),
         "reduce_scatter": lambda b: ar.reduce_scatter(b),
@@ -217,6 +223,10 @@ def run_one(args):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
+    # collect garbage now (earlier runs free large host arrays) and keep the
+    # collector out of the timed loop, which small workloads make host-bound
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -227,15 +237,16 @@ def run_one(args):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     event_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     finite = bool(all(torch.isfinite(b[:1 << 20].float()).all().item() for b in bufs[:2]))
     del flush_buf
 
     launch_ms = sum(event_ms) / len(event_ms)
     per_call_s = (launch_ms * 1e-3) if args.flush_mall else wall / args.steps
-    alg = algorithmic_bytes(args.collective, n, t, isz)
-    launches = 1 if args.impl == "fused" else ar.expected_steps(args.collective, n)
-    moved = alg if args.impl == "fused" else step_bytes(args.collective, n, t, isz)
+    alg = algorithmic_bytes(ran, n, t, isz)
+    launches = 1 if args.impl == "fused" else ar.expected_steps(ran, n)
+    moved = alg if args.impl == "fused" else step_bytes(ran, n, t, isz)
     achieved = moved / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(w.name, args.collective, args.impl)
 
@@ -252,7 +263,8 @@ def run_one(args):
         "vs_baseline": None,
         "dtype": DTYPE_TAG[w.dtype],
         "data": "synthetic",
-        "config": {"workload": w.name, "collective": args.collective, "impl": args.impl,
+        "config": {"workload": w.name, "collective": args.collective, "ran": ran,
+                   "impl": args.impl,
                    "nranks": n, "count_per_rank": t, "rank_bytes": t * isz,
                    "distribution": w.dist, "params": w.params, "seed": w.seed,
                    "timing": "events, Infinity Cache flushed before each call"
@@ -265,7 +277,7 @@ def run_one(args):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": KERNEL.get((args.collective, args.impl), "step_kernel"),
+            "kernel": KERNEL.get((ran, args.impl), "step_kernel"),
             "algorithmic_bytes_per_launch": moved if launches == 1 else None,
             "algorithmic_bytes_per_call": moved,
             "launches_per_step": launches,
@@ -304,8 +316,7 @@ def run_one(args):
         got = [p.clone() for p in pristine]
         call(got)
         torch.cuda.synchronize()
-        secs, compared, bad = run_checker(args.collective, pristine, got, w, args.root,
-                                          args.cpu_window)
+        secs, compared, bad = run_checker(ran, pristine, got, w, args.root, args.cpu_window)
         del pristine, got
         torch.cuda.empty_cache()
         windows = -(-t // args.cpu_window)
@@ -316,7 +327,7 @@ def run_one(args):
             "unit": "GB/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": f"the whole workload: {args.collective} of N={n} ranks x T={t} "
+            "sample": f"the whole workload: {ran} of N={n} ranks x T={t} "
                       f"{w.dtype} elements, run as {windows} windows of up to "
                       f"{args.cpu_window} elements per rank (literal NumPy simulation of "
                       f"the schedule, one thread), {secs:.2f} s",
@@ -346,9 +357,11 @@ SUITE = [
     ("small_int32", "allgather", "fused", ["--steps", "30"]),
     ("small_int32", "ring_allreduce", "step", ["--steps", "30"]),
 ] + [
-    (f"sweep_{t}", coll, impl, ["--steps", "30"] + (["--flush-mall"] if t >= 262_144 else []))
+    # message-size sweep: every size event-timed with the Infinity Cache flushed,
+    # so that the events hold GPU time only (the cost model is fitted to these)
+    (f"sweep_{t}", coll, impl, ["--steps", "30", "--flush-mall"])
     for t in (256, 262_144, 4_194_304, 67_108_864)
-    for coll in ("ring_allreduce", "tree_allreduce")
+    for coll in ("ring_allreduce", "tree_allreduce", "allreduce")
     for impl in ("fused", "step")
 ]
 

@@ -145,6 +145,40 @@ ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t
 ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
                               ar_op_t op, void* stream);
 
+/* ---- size-based choice between ring and tree ----------------------------- */
+
+/* AllReduce that picks the ring or the double tree by message size [L09 5.3:
+ * NCCL runs the tree for small messages and the ring for large ones][SCR
+ * exercises: ring vs tree at 1 KB, 1 MB and 16 MB].  It predicts the time of
+ * both under the current implementation (ar_set_impl) with the cost model
+ * below and runs ar_ring_allreduce or ar_tree_allreduce, whichever is lower
+ * (the ring on a tie).  Arguments, errors and counters are those of the call
+ * it runs; its result is that call's result bit for bit. */
+ar_status_t ar_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                         ar_op_t op, void* stream);
+
+/* The collective ar_allreduce would run (AR_RING_ALLREDUCE or
+ * AR_TREE_ALLREDUCE) for these arguments under the current implementation.
+ * Host only. */
+ar_status_t ar_allreduce_choice(int nranks, size_t count, ar_dtype_t dtype,
+                                ar_collective_t* choice);
+
+/* Cost model, the single-GPU form of the pages' alpha-beta model [L09 1.3,
+ * 7.3]: predicted microseconds of one call
+ *     = launches * alpha_us + hbm_bytes / (gbps * 1e3)
+ * where launches is 1 for AR_IMPL_FUSED and the schedule's step count for
+ * AR_IMPL_STEP, and hbm_bytes is what that implementation moves (fused:
+ * 2 N T s for an AllReduce; step: 3 bytes per element of every reduce
+ * transfer and 2 per element of every copy transfer).  One (alpha_us, gbps)
+ * pair is kept per (collective, implementation); the defaults are fitted to
+ * the message-size sweep measured on MI355X.  Host only. */
+ar_status_t ar_predict_time(ar_collective_t coll, ar_impl_t impl, int nranks, size_t count,
+                            ar_dtype_t dtype, double* microseconds);
+ar_status_t ar_set_cost_model(ar_collective_t coll, ar_impl_t impl, double alpha_us,
+                              double gbps);
+ar_status_t ar_get_cost_model(ar_collective_t coll, ar_impl_t impl, double* alpha_us,
+                              double* gbps);
+
 /* ---- host-only helpers: no GPU work, usable without a GPU ---------------- */
 
 /* C = ceil(count / nranks); 0 if nranks < 1. */

@@ -179,3 +179,106 @@ def test_host_helpers_reject_bad_arguments():
     assert lib.ar_expected_steps(0, 0) == -1 and lib.ar_expected_steps(0, 65) == -1
     assert lib.ar_counters_read(65, None, None, None) == 1
     assert lib.ar_chunk_size(0, 10) == 0
+
+
+# --- cost model and the size-based ring/tree choice -----------------------------
+
+def _oracle_hbm_bytes(coll, impl, n, t, dtype):
+    """HBM bytes of one call from the oracle's literal schedule: the fused
+    kernels move each input once and each output once; the step-by-step
+    implementation moves 3 bytes per element of every reduce transfer and 2
+    per element of every copy transfer."""
+    s = 2 if dtype == "bfloat16" else 4
+    if n == 1:
+        return 0
+    if impl == "fused":
+        return {"ring_allreduce": 2 * n * t, "tree_allreduce": 2 * n * t,
+                "reduce_scatter": (n + 1) * t, "allgather": n * t, "broadcast": n * t}[coll] * s
+    x = [np.zeros(t, np.int32) for _ in range(n)]
+    moved = int(sum(ORACLE_CALLS[coll](x, 0).sent)) // 4       # elements transferred
+    reduced = {"ring_allreduce": moved // 2, "tree_allreduce": moved // 2,
+               "reduce_scatter": moved}.get(coll, 0)
+    return (3 * reduced + 2 * (moved - reduced)) * s
+
+
+@pytest.mark.parametrize("coll", sorted(ORACLE_CALLS))
+@pytest.mark.parametrize("impl", ["fused", "step"])
+@pytest.mark.parametrize("n,t,dtype", [(4, 256, "float32"), (8, 100_003, "bfloat16"),
+                                       (64, 1_000_003, "float32"), (2, 7, "int32")])
+def test_predicted_time_is_the_documented_formula(coll, impl, n, t, dtype):
+    alpha, gbps = ar.get_cost_model(coll, impl)
+    launches = 1 if impl == "fused" else ar.expected_steps(coll, n)
+    want = launches * alpha + _oracle_hbm_bytes(coll, impl, n, t, dtype) / (gbps * 1e3)
+    assert ar.predict_time(coll, impl, n, t, dtype) == pytest.approx(want, rel=1e-12)
+
+
+def test_allreduce_choice_switches_at_the_model_crossover():
+    """With the step implementation on one GPU ring and tree move the same
+    HBM bytes (5 (N-1) T s), so the tree (2 ceil(log2 N) launches) beats the
+    ring (2 (N-1) launches) unless its bandwidth is lower.  Give the tree a
+    lower bandwidth: it must win below the analytic crossover size and lose
+    above it."""
+    saved = {(c, i): ar.get_cost_model(c, i) for c in ("ring_allreduce", "tree_allreduce")
+             for i in ("fused", "step")}
+    old = ar.get_impl()
+    try:
+        ar.set_impl("step")
+        ar.set_cost_model("ring_allreduce", "step", 4.0, 6000.0)
+        ar.set_cost_model("tree_allreduce", "step", 4.0, 5000.0)
+        n, s = 8, 4
+        # ring 14 a + 35 T s / 6000e3 = tree 6 a + 35 T s / 5000e3  ->  T*
+        t_star = (14 - 6) * 4.0 / (35 * s / 5000e3 - 35 * s / 6000e3)
+        below, above = int(t_star * 0.9), int(t_star * 1.1)
+        assert ar.allreduce_choice(n, below, "float32") == "tree_allreduce"
+        assert ar.allreduce_choice(n, above, "float32") == "ring_allreduce"
+        # equal predictions pick the ring
+        ar.set_cost_model("tree_allreduce", "step", 4.0 * 14 / 6, 6000.0)
+        assert ar.allreduce_choice(n, 1000, "float32") == "ring_allreduce"
+        ar.set_impl("fused")
+        ar.set_cost_model("ring_allreduce", "fused", 3.0, 6000.0)
+        ar.set_cost_model("tree_allreduce", "fused", 2.0, 5000.0)
+        assert ar.allreduce_choice(4, 256, "float32") == "tree_allreduce"
+        assert ar.allreduce_choice(4, 1 << 26, "float32") == "ring_allreduce"
+    finally:
+        for (c, i), (a, g) in saved.items():
+            ar.set_cost_model(c, i, a, g)
+        ar.set_impl(old)
+
+
+def test_cost_model_arguments_are_validated():
+    lib = ar.lib()
+    assert lib.ar_set_cost_model(7, 0, 1.0, 1.0) == binding.INVALID_ARGUMENT
+    assert lib.ar_set_cost_model(0, 3, 1.0, 1.0) == binding.INVALID_ARGUMENT
+    assert lib.ar_set_cost_model(0, 0, -1.0, 1.0) == binding.INVALID_ARGUMENT
+    assert lib.ar_set_cost_model(0, 0, 1.0, 0.0) == binding.INVALID_ARGUMENT
+    assert lib.ar_set_cost_model(0, 0, float("nan"), 1.0) == binding.INVALID_ARGUMENT
+    out = ctypes.c_int()
+    assert lib.ar_allreduce_choice(0, 10, 1, ctypes.byref(out)) == binding.INVALID_ARGUMENT
+    assert lib.ar_allreduce_choice(4, 10, 9, ctypes.byref(out)) == binding.INVALID_ARGUMENT
+    assert lib.ar_allreduce_choice(4, 10, 1, None) == binding.INVALID_ARGUMENT
+    us = ctypes.c_double()
+    assert lib.ar_predict_time(0, 0, 65, 10, 1, ctypes.byref(us)) == binding.INVALID_ARGUMENT
+    assert _call("allreduce", _fake(65)) == binding.INVALID_ARGUMENT
+    assert _call("allreduce", _fake(4, offset=2)) == binding.INVALID_ARGUMENT
+    assert _call("allreduce", _fake(4), count=0) == binding.SUCCESS
+
+
+def test_costfit_recovers_known_coefficients():
+    from tree_allreduce_algorithms_amd import costfit
+    truth = {("ring_allreduce", "step"): (3.7, 6100.0), ("tree_allreduce", "fused"): (2.5, 5600.0)}
+    records = []
+    for (coll, impl), (alpha, gbps) in truth.items():
+        for launches, nbytes in ((6, 15_360), (6, 15_728_640), (6, 251_658_240), (6, 4.0e9),
+                                 (1, 8_192), (1, 2.1e9)):
+            if impl == "fused":
+                launches = 1
+            us = launches * alpha + nbytes / (gbps * 1e3)
+            records.append({"config": {"collective": coll, "impl": impl,
+                                       "timing": "events, Infinity Cache flushed"},
+                            "roofline": {"launches_per_step": launches,
+                                         "algorithmic_bytes_per_call": nbytes,
+                                         "event_ms_mean": us / 1e3}})
+    got = costfit.fit(records)
+    for key, (alpha, gbps) in truth.items():
+        assert got[key][0] == pytest.approx(alpha, rel=1e-9)
+        assert got[key][1] == pytest.approx(gbps, rel=1e-9)

@@ -499,3 +499,35 @@ def test_graph_capture_replays_match_eager(coll, impl):
                 assert_same(got, want[r], "float32", f"replay {replay} rank {r}")
     del graph
     ar.set_impl("fused")
+
+
+# --- size-based ring / tree choice ------------------------------------------------
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_allreduce_runs_the_chosen_algorithm(impl):
+    """ar_allreduce runs whichever of ring and tree the cost model picks; its
+    output must equal the oracle of that algorithm bit for bit.  The model is
+    forced each way to cover both branches."""
+    n, t = 8, 50_001
+    x = workloads.host_inputs(n, t, "float32", "normal", 71, {"std": 1.0})
+    saved = {c: ar.get_cost_model(c, impl) for c in ("ring_allreduce", "tree_allreduce")}
+    ar.set_impl(impl)
+    try:
+        for favour in ("ring_allreduce", "tree_allreduce"):
+            other = "tree_allreduce" if favour == "ring_allreduce" else "ring_allreduce"
+            ar.set_cost_model(favour, impl, 0.0, 1e9)
+            ar.set_cost_model(other, impl, 1e6, 1.0)
+            assert ar.allreduce_choice(n, t, "float32") == favour
+            want = CALLS[favour][1](x, "sum", "float32", 0).bufs
+            bufs = to_dev(x, "float32")
+            ar.reset_counters()
+            ar.allreduce(bufs)
+            torch.cuda.synchronize()
+            for r in range(n):
+                assert_same(to_host(bufs[r], "float32"), want[r], "float32",
+                            f"allreduce->{favour}/{impl} rank {r}")
+            assert ar.counters(n)[:2] == ar.expected_bytes(favour, n, t, "float32")
+    finally:
+        for c, (a, g) in saved.items():
+            ar.set_cost_model(c, impl, a, g)
+        ar.set_impl("fused")

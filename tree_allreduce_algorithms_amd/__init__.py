@@ -9,18 +9,23 @@ it has not been built the call raises.
 from .binding import (  # noqa: F401
     ArError,
     allgather,
+    allreduce,
+    allreduce_choice,
     broadcast,
     chunk_range,
     chunk_size,
     counters,
     expected_bytes,
     expected_steps,
+    get_cost_model,
     get_impl,
     lib,
+    predict_time,
     raw_call,
     reduce_scatter,
     reset_counters,
     ring_allreduce,
+    set_cost_model,
     set_impl,
     tree_allreduce,
 )

@@ -30,6 +30,12 @@ SIGNATURES = {
     "ar_allgather": (_I, [_PP, _I, _SZ, _I, _VP]),
     "ar_broadcast": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
     "ar_tree_allreduce": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_allreduce": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_allreduce_choice": (_I, [_I, _SZ, _I, ctypes.POINTER(_I)]),
+    "ar_predict_time": (_I, [_I, _I, _I, _SZ, _I, ctypes.POINTER(ctypes.c_double)]),
+    "ar_set_cost_model": (_I, [_I, _I, ctypes.c_double, ctypes.c_double]),
+    "ar_get_cost_model": (_I, [_I, _I, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_double)]),
     "ar_chunk_size": (_SZ, [_I, _SZ]),
     "ar_chunk_range": (_I, [_I, _SZ, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "ar_expected_bytes": (_I, [_I, _I, _SZ, _I, _I, _U64P, _U64P]),
@@ -94,7 +100,7 @@ def raw_call(name, ptrs, count, dtype, op=None, root=None, stream=0):
     n = len(ptrs)
     fn = getattr(lib(), "ar_" + name)
     dt = DTYPES[dtype]
-    if name in ("ring_allreduce", "reduce_scatter", "tree_allreduce"):
+    if name in ("ring_allreduce", "reduce_scatter", "tree_allreduce", "allreduce"):
         status = fn(pp, n, count, dt, OPS[op], stream)
     elif name == "allgather":
         status = fn(pp, n, count, dt, stream)
@@ -174,7 +180,42 @@ def tree_allreduce(tensors, op="sum", stream=None):
     return _collective("tree_allreduce", tensors, op=op, stream=stream)
 
 
+def allreduce(tensors, op="sum", stream=None):
+    """AllReduce in place by the ring or the double tree, whichever the cost
+    model predicts faster for this size (see ar_allreduce)."""
+    return _collective("allreduce", tensors, op=op, stream=stream)
+
+
 # --- host-only helpers --------------------------------------------------------
+
+def allreduce_choice(nranks, count, dtype):
+    """'ring_allreduce' or 'tree_allreduce': what allreduce() would run."""
+    out = ctypes.c_int()
+    _check(lib().ar_allreduce_choice(nranks, count, DTYPES[dtype], ctypes.byref(out)),
+           "allreduce_choice")
+    return {v: k for k, v in COLLECTIVES.items()}[out.value]
+
+
+def predict_time(collective, impl, nranks, count, dtype):
+    """Cost-model prediction of one call, in microseconds."""
+    us = ctypes.c_double()
+    _check(lib().ar_predict_time(COLLECTIVES[collective], IMPLS[impl], nranks, count,
+                                 DTYPES[dtype], ctypes.byref(us)), "predict_time")
+    return us.value
+
+
+def get_cost_model(collective, impl):
+    """(alpha_us per launch, GB/s of HBM traffic) for this collective and impl."""
+    a, g = ctypes.c_double(), ctypes.c_double()
+    _check(lib().ar_get_cost_model(COLLECTIVES[collective], IMPLS[impl], ctypes.byref(a),
+                                   ctypes.byref(g)), "get_cost_model")
+    return a.value, g.value
+
+
+def set_cost_model(collective, impl, alpha_us, gbps):
+    _check(lib().ar_set_cost_model(COLLECTIVES[collective], IMPLS[impl], float(alpha_us),
+                                   float(gbps)), "set_cost_model")
+
 
 def chunk_size(nranks, count):
     return lib().ar_chunk_size(nranks, count)

@@ -31,6 +31,47 @@ std::atomic<int> g_impl{static_cast<int>(impl_from_env())};
 
 thread_local int t_last_hip_error = 0;
 
+// Cost model coefficients (alpha_us per launch, gbps of HBM traffic) per
+// collective and implementation.  The AllReduce pairs are the least-squares
+// fit of launches * alpha + bytes / gbps to the N=4 float32 message-size sweep
+// (1 KiB to 256 MiB per rank, Infinity Cache flushed before every call) on one
+// MI355X.  ReduceScatter, AllGather and Broadcast were measured at one size
+// (N=64, 64 MB per rank), which fixes their bandwidth; they take the
+// AllReduce fit's per-launch alpha.
+struct CostCoeff {
+  double alpha_us;
+  double gbps;
+};
+std::mutex g_cost_mu;
+CostCoeff g_cost[5][2] = {
+    {{6.18, 5905.0}, {3.16, 6186.0}},   // ring AllReduce: fused, step
+    {{6.18, 5721.0}, {3.16, 5243.0}},   // ReduceScatter
+    {{6.18, 4940.0}, {3.16, 4609.0}},   // AllGather
+    {{6.18, 5052.0}, {3.16, 5790.0}},   // Broadcast
+    {{6.21, 5825.0}, {3.24, 6090.0}},   // double-tree AllReduce
+};
+
+bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_TREE_ALLREDUCE; }
+bool impl_ok(int impl) { return impl == AR_IMPL_FUSED || impl == AR_IMPL_STEP; }
+
+double predict_us(ar_collective_t coll, ar_impl_t impl, int n, size_t count, ar_dtype_t dtype) {
+  CostCoeff c;
+  {
+    std::lock_guard<std::mutex> lock(g_cost_mu);
+    c = g_cost[coll][impl];
+  }
+  const double launches = ar::impl_launches(coll, impl, n);
+  const double bytes = static_cast<double>(ar::impl_hbm_bytes(coll, impl, n, count, ar::itemsize(dtype)));
+  return launches * c.alpha_us + bytes / (c.gbps * 1e3);
+}
+
+ar_collective_t choose_allreduce(int n, size_t count, ar_dtype_t dtype) {
+  const ar_impl_t impl = static_cast<ar_impl_t>(g_impl.load());
+  const double ring = predict_us(AR_RING_ALLREDUCE, impl, n, count, dtype);
+  const double tree = predict_us(AR_TREE_ALLREDUCE, impl, n, count, dtype);
+  return tree < ring ? AR_TREE_ALLREDUCE : AR_RING_ALLREDUCE;
+}
+
 void add_counters(ar_collective_t coll, const std::vector<ar::Step>& sched, int n, size_t isz) {
   uint64_t sent[AR_MAX_RANKS] = {};
   uint64_t recv[AR_MAX_RANKS] = {};
@@ -133,6 +174,48 @@ ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dt
                               ar_op_t op, void* stream) {
   if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_TREE_ALLREDUCE, bufs, nranks, count, dtype, static_cast<int>(op), -1, stream);
+}
+
+ar_status_t ar_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, ar_op_t op,
+                         void* stream) {
+  if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > AR_MAX_RANKS || !ar::dtype_ok(static_cast<int>(dtype)))
+    return AR_ERROR_INVALID_ARGUMENT;
+  return run(choose_allreduce(nranks, count, dtype), bufs, nranks, count, dtype,
+             static_cast<int>(op), -1, stream);
+}
+
+ar_status_t ar_allreduce_choice(int nranks, size_t count, ar_dtype_t dtype, ar_collective_t* choice) {
+  if (nranks < 1 || nranks > AR_MAX_RANKS || !ar::dtype_ok(static_cast<int>(dtype)) ||
+      choice == nullptr)
+    return AR_ERROR_INVALID_ARGUMENT;
+  *choice = choose_allreduce(nranks, count, dtype);
+  return AR_SUCCESS;
+}
+
+ar_status_t ar_predict_time(ar_collective_t coll, ar_impl_t impl, int nranks, size_t count,
+                            ar_dtype_t dtype, double* microseconds) {
+  if (!coll_ok(coll) || !impl_ok(impl) || nranks < 1 || nranks > AR_MAX_RANKS ||
+      !ar::dtype_ok(static_cast<int>(dtype)) || microseconds == nullptr)
+    return AR_ERROR_INVALID_ARGUMENT;
+  *microseconds = predict_us(coll, impl, nranks, count, dtype);
+  return AR_SUCCESS;
+}
+
+ar_status_t ar_set_cost_model(ar_collective_t coll, ar_impl_t impl, double alpha_us, double gbps) {
+  if (!coll_ok(coll) || !impl_ok(impl) || !(alpha_us >= 0.0) || !(gbps > 0.0))
+    return AR_ERROR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lock(g_cost_mu);
+  g_cost[coll][impl] = {alpha_us, gbps};
+  return AR_SUCCESS;
+}
+
+ar_status_t ar_get_cost_model(ar_collective_t coll, ar_impl_t impl, double* alpha_us, double* gbps) {
+  if (!coll_ok(coll) || !impl_ok(impl)) return AR_ERROR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lock(g_cost_mu);
+  if (alpha_us != nullptr) *alpha_us = g_cost[coll][impl].alpha_us;
+  if (gbps != nullptr) *gbps = g_cost[coll][impl].gbps;
+  return AR_SUCCESS;
 }
 
 size_t ar_chunk_size(int nranks, size_t count) {

@@ -147,6 +147,30 @@ int expected_steps(ar_collective_t coll, int n) {
   return -1;
 }
 
+int impl_launches(ar_collective_t coll, ar_impl_t impl, int n) {
+  if (impl == AR_IMPL_FUSED) return n > 1 ? 1 : 0;
+  return expected_steps(coll, n);
+}
+
+uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz) {
+  if (n <= 1) return 0;
+  const uint64_t un = static_cast<uint64_t>(n);
+  if (impl == AR_IMPL_FUSED) {
+    switch (coll) {
+      case AR_RING_ALLREDUCE:
+      case AR_TREE_ALLREDUCE: return 2 * un * count * isz;
+      case AR_REDUCE_SCATTER: return (un + 1) * count * isz;
+      case AR_ALLGATHER:
+      case AR_BROADCAST: return un * count * isz;
+    }
+    return 0;
+  }
+  uint64_t bytes = 0;
+  for (const Step& s : schedule_for(coll, n, count, 0))
+    for (const Transfer& x : s.xfers) bytes += (x.hi - x.lo) * isz * (s.reduce ? 3 : 2);
+  return bytes;
+}
+
 ar_status_t validate(void* const* bufs, int n, size_t count, int dtype, int op, int root) {
   if (!dtype_ok(dtype)) return AR_ERROR_INVALID_ARGUMENT;
   if (op >= 0 && !op_ok(op)) return AR_ERROR_INVALID_ARGUMENT;

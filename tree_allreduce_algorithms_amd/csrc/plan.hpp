@@ -55,6 +55,15 @@ void count_bytes(const std::vector<Step>& steps, size_t isz, uint64_t* sent, uin
 
 int expected_steps(ar_collective_t coll, int n);
 
+// Kernel launches and HBM bytes of one call of `coll` with implementation
+// `impl`: the fused kernels run once and move the algorithmic bytes (every
+// input read once, every output written once); the step implementation
+// launches once per schedule step and moves 3 bytes per element of each
+// reduce transfer (read both sides, write one) and 2 per element of each copy
+// transfer.
+int impl_launches(ar_collective_t coll, ar_impl_t impl, int n);
+uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz);
+
 // Validation shared by every collective call.  `op` < 0 means "not used",
 // `root` < 0 means "not used".  Checks: bufs / entries non-NULL, n in range,
 // element alignment, count * itemsize overflow, pairwise overlap of the
