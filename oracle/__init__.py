@@ -22,6 +22,8 @@ Sources (cited by page title and section):
   communication patterns), sections 4.3.1 (ring pseudo-code) and 4.3.2 (tree).
 * "从零实现集合通信" (Collectives from scratch), section "两趟实现 ring
   allreduce" (two-pass ring) and its per-primitive cost table.
+* Lecture 09 sections 3.2-3.4 for Scatter, Gather and Reduce (each rank not
+  named as receiving keeps its data).
 
 Pins (what the oracle is checked against in ``tests/test_oracle_*.py``):
 int32 brute force, hand-derived order-revealing fp32 examples, the worked
@@ -47,8 +49,11 @@ from .collectives import (  # noqa: F401
     broadcast,
     ceil_log2,
     chunk_layout,
+    gather,
+    reduce,
     ring_allgather,
     ring_allreduce,
     ring_reduce_scatter,
+    scatter,
     tree_allreduce,
 )

@@ -84,6 +84,12 @@ def ag_send_chunk(r, t, n):
     return (r - t) % n
 
 
+def rooted_rank(role, root, n):
+    """Rank playing ``role`` in a tree rooted at ``root``: roles are ranks
+    counted from the root, (rank - root) mod N (Broadcast, Reduce)."""
+    return (role + root) % n
+
+
 def tree_rank(tree, role, n):
     """Rank playing ``role`` in tree 0 (identity) or tree 1 (mirror N-1-role).
 
@@ -264,10 +270,77 @@ def broadcast(x, root, dtype, window_start=0, total=None):
         packets = []
         for q in range(0, n, 2 * stride):
             if q + stride < n:
-                src = (q + root) % n
-                dst = (q + stride + root) % n
+                src = rooted_rank(q, root, n)
+                dst = rooted_rank(q + stride, root, n)
                 packets.append((src, dst, bufs[src][whole].copy()))
         for src, dst, payload in packets:
             bufs[dst][whole] = payload
             _count(sent, recv, src, dst, payload.size, dtype)
     return Result(bufs, sent, recv, depth)
+
+
+# --- rooted primitives: Reduce, Scatter, Gather --------------------------------
+
+def reduce(x, root, op, dtype, window_start=0, total=None):
+    """Reduce to ``root`` (Lecture 09, section 3.4): the root ends with the
+    reduction of every rank's buffer and every other rank keeps its data.
+
+    Order: the reduce rounds of a binomial tree on roles (rank - root) mod N,
+    the same rounds the tree AllReduce runs (Lecture 09 section 5.2; cost
+    table of "Collectives from scratch": log2 N tree steps).  Every rank works
+    on a copy of its buffer (the receive buffer of a real rank); round k
+    (k = 0, 1, ...): role q with q mod 2^(k+1) == 0 and q + 2^k < N receives
+    the working copy of role q + 2^k and stores own (+) received.  At the end
+    the root's buffer takes the root's working copy; the other buffers are
+    unchanged, as section 3.4 requires.
+    """
+    n, length, total, bufs, sent, recv = _setup(x, dtype, window_start, total)
+    if not 0 <= root < n:
+        raise ValueError("root out of range")
+    work = [b.copy() for b in bufs]
+    depth = ceil_log2(n)
+    for k in range(depth):
+        stride = 1 << k
+        packets = []
+        for q in range(0, n, 2 * stride):
+            if q + stride < n:
+                src = rooted_rank(q + stride, root, n)
+                dst = rooted_rank(q, root, n)
+                packets.append((src, dst, work[src].copy()))
+        for src, dst, payload in packets:
+            work[dst] = combine(work[dst], payload, op, dtype)
+            _count(sent, recv, src, dst, payload.size, dtype)
+    bufs[root] = work[root]
+    return Result(bufs, sent, recv, depth)
+
+
+def scatter(x, root, dtype, window_start=0, total=None):
+    """Scatter from ``root`` (Lecture 09, section 3.2): the root's buffer is
+    cut into the N ring chunks and chunk c goes to rank c, in place of rank
+    c's chunk c.  One step of N-1 direct transfers; every other element of
+    every buffer (the root's whole buffer included) is unchanged."""
+    n, length, total, bufs, sent, recv = _setup(x, dtype, window_start, total)
+    if not 0 <= root < n:
+        raise ValueError("root out of range")
+    span = _ring_spans(n, total, window_start, length)
+    packets = [(c, bufs[root][span[c]].copy()) for c in range(n) if c != root]
+    for c, payload in packets:
+        bufs[c][span[c]] = payload
+        _count(sent, recv, root, c, payload.size, dtype)
+    return Result(bufs, sent, recv, 1 if n > 1 else 0)
+
+
+def gather(x, root, dtype, window_start=0, total=None):
+    """Gather to ``root`` (Lecture 09, section 3.3): rank c's chunk c lands in
+    chunk c of the root's buffer, so the root holds every rank's shard in
+    rank order.  One step of N-1 direct transfers; the other ranks keep
+    their data."""
+    n, length, total, bufs, sent, recv = _setup(x, dtype, window_start, total)
+    if not 0 <= root < n:
+        raise ValueError("root out of range")
+    span = _ring_spans(n, total, window_start, length)
+    packets = [(c, bufs[c][span[c]].copy()) for c in range(n) if c != root]
+    for c, payload in packets:
+        bufs[root][span[c]] = payload
+        _count(sent, recv, c, root, payload.size, dtype)
+    return Result(bufs, sent, recv, 1 if n > 1 else 0)

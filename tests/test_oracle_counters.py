@@ -128,3 +128,30 @@ def test_step_counts_ring_vs_tree(n, ring, tree):
     if n <= 64:
         assert oracle.ring_allreduce([np.zeros(2, np.float32)] * n, "sum", "float32").steps == ring
     assert 2 * (n - 1) == ring
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 13, 64])
+@pytest.mark.parametrize("t", [0, 7, 1000])
+def test_rooted_primitive_bytes(n, t):
+    """Reduce: every non-root role sends its whole buffer once (to its parent
+    in the binomial tree), the root receives one buffer per child, i.e.
+    ceil(log2 N) of them [cost table, log2 N tree steps].  Scatter / Gather:
+    each non-root rank receives / sends exactly its own chunk."""
+    x = [np.zeros(t, np.int32) for _ in range(n)]
+    layout = oracle.chunk_layout(n, t)
+    for root in sorted({0, n - 1}):
+        red = oracle.reduce(x, root, "sum", "int32")
+        assert red.steps == oracle.ceil_log2(n)
+        assert int(red.recv[root]) == 4 * t * oracle.ceil_log2(n)
+        assert int(red.sent.sum()) == 4 * t * (n - 1)
+        assert all(int(red.sent[r]) == 4 * t for r in range(n) if r != root)
+        assert int(red.sent[root]) == 0
+        sc = oracle.scatter(x, root, "int32")
+        ga = oracle.gather(x, root, "int32")
+        for r in range(n):
+            size = 4 * (layout[r][1] - layout[r][0])
+            if r != root:
+                assert int(sc.recv[r]) == size and int(ga.sent[r]) == size
+        own = 4 * (layout[root][1] - layout[root][0])
+        assert int(sc.sent[root]) == 4 * t - own == int(ga.recv[root])
+        assert sc.steps == ga.steps == (1 if n > 1 else 0)

@@ -40,6 +40,13 @@ def _pins_hold():
         tr = oracle.tree_allreduce(x, "sum", "int32")
         if any(not np.array_equal(b, want) for b in tr.bufs):
             return False
+        root = n - 1
+        red = oracle.reduce(x, root, "sum", "int32")
+        if not np.array_equal(red.bufs[root], want) or int(red.sent[root]) != 0:
+            return False
+        bc = oracle.broadcast(x, root, "int32")
+        if any(not np.array_equal(b, x[root]) for b in bc.bufs) or int(bc.recv[root]) != 0:
+            return False
     with open(os.path.join(GOLDEN, "order_examples.json")) as f:
         for case in json.load(f)["cases"]:
             x = [np.array(v, dtype=np.float32) for v in case["inputs"]]
@@ -62,6 +69,7 @@ MUTATIONS = {
     "ring_skips_a_neighbour": ("ring_next", lambda r, n: (r + 2) % n),
     "ring_turns_left": ("ring_next", lambda r, n: (r - 1) % n),
     "tree_one_not_mirrored": ("tree_rank", lambda tree, role, n: role),
+    "rooted_tree_ignores_root": ("rooted_rank", lambda role, root, n: role),
     "receiver_overwrites_instead_of_adding": (
         "combine", lambda local, incoming, op, dtype: np.array(incoming, copy=True)),
     "receiver_drops_incoming": ("combine", lambda local, incoming, op, dtype: np.array(local, copy=True)),

@@ -44,6 +44,12 @@ def _run(case, x):
         return oracle.tree_allreduce(x, case["op"], dtype)
     if coll == "broadcast":
         return oracle.broadcast(x, case["root"], dtype)
+    if coll == "reduce":
+        return oracle.reduce(x, case["root"], case["op"], dtype)
+    if coll == "scatter":
+        return oracle.scatter(x, case["root"], dtype)
+    if coll == "gather":
+        return oracle.gather(x, case["root"], dtype)
     raise AssertionError(coll)
 
 
@@ -331,3 +337,69 @@ def test_inputs_are_not_modified():
     oracle.tree_allreduce(x, "sum", "float32")
     for a, b in zip(x, keep):
         np.testing.assert_array_equal(a, b)
+
+
+# --- Reduce, Scatter, Gather (Lecture 09 sections 3.2-3.4) ---------------------
+
+@pytest.mark.parametrize("n,t", SHAPES)
+@pytest.mark.parametrize("op", ["sum", "prod", "max", "min"])
+def test_int32_reduce_brute_force_and_others_unchanged(n, t, op):
+    x = _ints(n, t, 5 * n + t + 1)
+    for root in sorted({0, n // 2, n - 1}):
+        res = oracle.reduce(x, root, op, "int32")
+        np.testing.assert_array_equal(res.bufs[root], _brute(x, op))
+        for r in range(n):
+            if r != root:
+                np.testing.assert_array_equal(res.bufs[r], x[r])
+
+
+def _binomial_fold_closed_form(vals, op_add):
+    """The binomial tree's reduce rounds written as a recursion over blocks of
+    roles: the block of 2^k roles starting at role q is its lower half (the
+    receiving side) combined with its upper half when the upper half has at
+    least one role."""
+    n = len(vals)
+
+    def block(q, k):
+        if k == 0:
+            return vals[q]
+        half = 1 << (k - 1)
+        low = block(q, k - 1)
+        return op_add(low, block(q + half, k - 1)) if q + half < n else low
+
+    return block(0, oracle.ceil_log2(n))
+
+
+@pytest.mark.parametrize("n,t", FP_SHAPES)
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_reduce_fold_order_closed_form(n, t, dtype):
+    x = _normals(n, t, 4000 + n * t, dtype)
+    if dtype == "float32":
+        add = lambda a, b: a + b
+    else:
+        def add(a, b):
+            widen = lambda u: torch.from_numpy(u.view(np.int16).copy()).view(torch.bfloat16).float()
+            s_ = (widen(a) + widen(b)).to(torch.bfloat16)
+            return s_.view(torch.int16).numpy().view(np.uint16)
+    for root in sorted({0, n - 1, n // 3}):
+        roles = [x[(q + root) % n] for q in range(n)]
+        want = _binomial_fold_closed_form(roles, add)
+        np.testing.assert_array_equal(oracle.reduce(x, root, "sum", dtype).bufs[root], want)
+
+
+@pytest.mark.parametrize("n,t", SHAPES)
+def test_scatter_and_gather_brute_force(n, t):
+    x = _ints(n, t, 9 * n + t)
+    layout = oracle.chunk_layout(n, t)
+    for root in sorted({0, n - 1}):
+        sc = oracle.scatter(x, root, "int32")
+        ga = oracle.gather(x, root, "int32")
+        for r in range(n):
+            want_sc = x[r].copy()
+            lo, hi = layout[r]
+            want_sc[lo:hi] = x[root][lo:hi]
+            np.testing.assert_array_equal(sc.bufs[r], want_sc)
+            if r != root:
+                np.testing.assert_array_equal(ga.bufs[r], x[r])
+        want_ga = np.concatenate([x[c][lo:hi] for c, (lo, hi) in enumerate(layout)]) if t else x[root]
+        np.testing.assert_array_equal(ga.bufs[root], want_ga)
