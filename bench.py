@@ -56,13 +56,15 @@ HBM_PEAK_GBPS = 8000.0
 DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
 MAX_CALLS = 35
 COLLECTIVES = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce",
-               "allreduce"]
+               "allreduce", "reduce", "scatter", "gather"]
 KERNEL = {  # collective, impl -> kernel that dominates one call
     ("ring_allreduce", "fused"): "ring_fold_kernel",
     ("reduce_scatter", "fused"): "ring_fold_kernel",
     ("allgather", "fused"): "fanout_kernel",
     ("broadcast", "fused"): "fanout_kernel",
     ("tree_allreduce", "fused"): "tree_fold_kernel",
+    ("reduce", "fused"): "tree_fold_kernel",
+    ("reduce", "step"): "tree_fold_kernel",   # Reduce has one (fused) implementation
 }
 
 
@@ -123,6 +125,10 @@ def algorithmic_bytes(collective, n, t, isz):
         "reduce_scatter": (n + 1) * t * isz,   # read N, write the owner's chunk
         "allgather": n * t * isz,              # read each chunk once, write N-1 copies
         "broadcast": n * t * isz,
+        "reduce": (n + 1) * t * isz,           # read N, write the root's buffer
+        # one chunk per non-root rank, read once and written once
+        "scatter": 2 * (t - -(-t // n)) * isz if n > 1 else 0,
+        "gather": 2 * (t - -(-t // n)) * isz if n > 1 else 0,
     }[collective]
 
 
@@ -133,6 +139,8 @@ def step_bytes(collective, n, t, isz):
     sent, _ = ar.expected_bytes(collective, n, t, "bfloat16" if isz == 2 else "int32")
     moved = sum(sent) // isz                     # elements transferred over all steps
     # share of those elements moved by reduce (rather than copy) transfers
+    if collective == "reduce":                   # one (fused) implementation
+        return algorithmic_bytes(collective, n, t, isz)
     reduce_share = {"ring_allreduce": (1, 2), "tree_allreduce": (1, 2),
                     "reduce_scatter": (1, 1)}.get(collective, (0, 1))
     reduced = moved * reduce_share[0] // reduce_share[1]
@@ -162,6 +170,9 @@ def run_checker(collective, pristine, got, w, root, window):
         "reduce_scatter": lambda x, a: oracle.ring_reduce_scatter(x, "sum", w.dtype, a, t),
         "allgather": lambda x, a: oracle.ring_allgather(x, w.dtype, a, t),
         "broadcast": lambda x, a: oracle.broadcast(x, root, w.dtype, a, t),
+        "reduce": lambda x, a: oracle.reduce(x, root, "sum", w.dtype, a, t),
+        "scatter": lambda x, a: oracle.scatter(x, root, w.dtype, a, t),
+        "gather": lambda x, a: oracle.gather(x, root, w.dtype, a, t),
     }[collective]
     secs, compared, bad = 0.0, 0, 0
     for a in range(0, t, window):
@@ -213,6 +224,9 @@ def run_one(args):
         "reduce_scatter": lambda b: ar.reduce_scatter(b),
         "allgather": lambda b: ar.allgather(b),
         "broadcast": lambda b: ar.broadcast(b, root=args.root),
+        "reduce": lambda b: ar.reduce(b, root=args.root),
+        "scatter": lambda b: ar.scatter(b, root=args.root),
+        "gather": lambda b: ar.gather(b, root=args.root),
     }[args.collective]
     stream = torch.cuda.current_stream(dev)
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_mall else None
@@ -245,7 +259,8 @@ def run_one(args):
     launch_ms = sum(event_ms) / len(event_ms)
     per_call_s = (launch_ms * 1e-3) if args.flush_mall else wall / args.steps
     alg = algorithmic_bytes(ran, n, t, isz)
-    launches = 1 if args.impl == "fused" else ar.expected_steps(ran, n)
+    launches = (1 if args.impl == "fused" or ran == "reduce"
+                else ar.expected_steps(ran, n))
     moved = alg if args.impl == "fused" else step_bytes(ran, n, t, isz)
     achieved = moved / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(w.name, args.collective, args.impl)
@@ -352,6 +367,10 @@ SUITE = [
     ("zero_n64", "reduce_scatter", "step", []),
     ("zero_n64", "allgather", "step", []),
     ("zero_n64", "broadcast", "step", []),
+    ("zero_n64", "reduce", "fused", []),
+    ("zero_n64", "scatter", "fused", []),
+    ("zero_n64", "gather", "fused", []),
+    ("large_grad_fp32", "reduce", "fused", []),
     ("small_int32", "ring_allreduce", "fused", ["--steps", "30"]),
     ("small_int32", "reduce_scatter", "fused", ["--steps", "30"]),
     ("small_int32", "allgather", "fused", ["--steps", "30"]),

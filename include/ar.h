@@ -95,7 +95,10 @@ typedef enum {
   AR_REDUCE_SCATTER = 1,
   AR_ALLGATHER = 2,
   AR_BROADCAST = 3,
-  AR_TREE_ALLREDUCE = 4
+  AR_TREE_ALLREDUCE = 4,
+  AR_REDUCE = 5,
+  AR_SCATTER = 6,
+  AR_GATHER = 7
 } ar_collective_t;
 
 /* How a collective is executed; results are bit-identical either way.
@@ -145,6 +148,34 @@ ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t
 ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
                               ar_op_t op, void* stream);
 
+/* ---- rooted primitives ------------------------------------------------------ */
+
+/* Reduce to `root` [L09 3.4]: bufs[root] ends with the reduction of every
+ * rank's buffer; every other buffer keeps its data.  Order: the reduce
+ * rounds of a binomial tree on roles (rank - root) mod N over the whole
+ * buffer (the rounds of ar_tree_allreduce [L09 5.2]): round k, role q
+ * (q mod 2^(k+1) == 0, q + 2^k < N) stores own (+) value of role q + 2^k;
+ * the partials live in registers, never in a rank buffer.  One fused kernel
+ * runs under either implementation.  Counters: each non-root rank sends its
+ * buffer once to its parent; ceil(log2 N) steps.  root out of range ->
+ * AR_ERROR_INVALID_ARGUMENT. */
+ar_status_t ar_reduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, ar_op_t op,
+                      int root, void* stream);
+
+/* Scatter from `root` [L09 3.2]: chunk c of bufs[root] (the ring chunk
+ * layout above) is copied into chunk c of bufs[c] for every c != root; every
+ * other element of every buffer is unchanged.  One step of N-1 direct
+ * transfers. */
+ar_status_t ar_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
+                       void* stream);
+
+/* Gather to `root` [L09 3.3]: chunk c of bufs[c] is copied into chunk c of
+ * bufs[root] for every c != root, so the root holds every rank's shard in
+ * rank order; the other buffers are unchanged.  One step of N-1 direct
+ * transfers. */
+ar_status_t ar_gather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
+                      void* stream);
+
 /* ---- size-based choice between ring and tree ----------------------------- */
 
 /* AllReduce that picks the ring or the double tree by message size [L09 5.3:
@@ -191,13 +222,14 @@ ar_status_t ar_chunk_range(int nranks, size_t count, int chunk, size_t* begin, s
 /* Logical bytes each rank sends and receives in one call of `coll` with these
  * arguments ([SCR cost table]; e.g. 2T(N-1)/N per rank for the ring when N
  * divides T).  sent and recv are caller arrays of nranks uint64_t.  `root`
- * is used for AR_BROADCAST only. */
+ * is used for AR_BROADCAST, AR_REDUCE, AR_SCATTER and AR_GATHER only. */
 ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype,
                               int root, uint64_t* sent, uint64_t* recv);
 
 /* Schedule steps of one call: 2(N-1) ring AllReduce, N-1 ReduceScatter and
- * AllGather, ceil(log2 N) Broadcast, 2 ceil(log2 N) tree AllReduce; -1 on a
- * bad argument. */
+ * AllGather, ceil(log2 N) Broadcast and Reduce, 2 ceil(log2 N) tree
+ * AllReduce, 1 Scatter and Gather (0 for every collective when N == 1); -1
+ * on a bad argument. */
 int ar_expected_steps(ar_collective_t coll, int nranks);
 
 /* Process-wide cumulative counters since load or the last reset.  Copies the

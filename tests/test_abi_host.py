@@ -65,6 +65,9 @@ ORACLE_CALLS = {
     "allgather": lambda x, root: oracle.ring_allgather(x, "int32"),
     "broadcast": lambda x, root: oracle.broadcast(x, root, "int32"),
     "tree_allreduce": lambda x, root: oracle.tree_allreduce(x, "sum", "int32"),
+    "reduce": lambda x, root: oracle.reduce(x, root, "sum", "int32"),
+    "scatter": lambda x, root: oracle.scatter(x, root, "int32"),
+    "gather": lambda x, root: oracle.gather(x, root, "int32"),
 }
 
 
@@ -106,7 +109,9 @@ def _fake(n, stride=1 << 20, offset=0):
     return [FAKE + offset + r * stride for r in range(n)]
 
 
-ALL = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce"]
+ALL = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce", "reduce",
+       "scatter", "gather"]
+ROOTED = ("broadcast", "reduce", "scatter", "gather")
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -127,9 +132,15 @@ def test_invalid_arguments(name):
         assert fn(pp, 4, 16, 7, 0, None) == inv                     # unknown dtype
         assert fn(pp, 4, 16, 1, 9, None) == inv                     # unknown op
         assert fn(None, 4, 16, 1, 0, None) == inv                   # NULL bufs
-    if name == "broadcast":
-        assert lib.ar_broadcast(pp, 4, 16, 1, 4, None) == inv       # root out of range
-        assert lib.ar_broadcast(pp, 4, 16, 1, -1, None) == inv
+    if name in ("broadcast", "scatter", "gather"):
+        fn = getattr(lib, "ar_" + name)
+        assert fn(pp, 4, 16, 1, 4, None) == inv                     # root out of range
+        assert fn(pp, 4, 16, 1, -1, None) == inv
+    if name == "reduce":
+        assert lib.ar_reduce(pp, 4, 16, 1, 0, 4, None) == inv       # root out of range
+        assert lib.ar_reduce(pp, 4, 16, 1, 0, -1, None) == inv
+        assert lib.ar_reduce(pp, 4, 16, 1, 9, 0, None) == inv       # unknown op
+        assert lib.ar_reduce(pp, 4, 16, 7, 0, 0, None) == inv       # unknown dtype
     del keep
 
 
@@ -191,7 +202,9 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
     s = 2 if dtype == "bfloat16" else 4
     if n == 1:
         return 0
-    if impl == "fused":
+    if coll == "reduce":                 # one fused implementation
+        return (n + 1) * t * s
+    if impl == "fused" and coll not in ("scatter", "gather"):
         return {"ring_allreduce": 2 * n * t, "tree_allreduce": 2 * n * t,
                 "reduce_scatter": (n + 1) * t, "allgather": n * t, "broadcast": n * t}[coll] * s
     x = [np.zeros(t, np.int32) for _ in range(n)]
@@ -207,7 +220,9 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
                                        (64, 1_000_003, "float32"), (2, 7, "int32")])
 def test_predicted_time_is_the_documented_formula(coll, impl, n, t, dtype):
     alpha, gbps = ar.get_cost_model(coll, impl)
-    launches = 1 if impl == "fused" else ar.expected_steps(coll, n)
+    launches = 1 if impl == "fused" or coll == "reduce" else ar.expected_steps(coll, n)
+    if n == 1:
+        launches = 0
     want = launches * alpha + _oracle_hbm_bytes(coll, impl, n, t, dtype) / (gbps * 1e3)
     assert ar.predict_time(coll, impl, n, t, dtype) == pytest.approx(want, rel=1e-12)
 
@@ -247,7 +262,7 @@ def test_allreduce_choice_switches_at_the_model_crossover():
 
 def test_cost_model_arguments_are_validated():
     lib = ar.lib()
-    assert lib.ar_set_cost_model(7, 0, 1.0, 1.0) == binding.INVALID_ARGUMENT
+    assert lib.ar_set_cost_model(8, 0, 1.0, 1.0) == binding.INVALID_ARGUMENT
     assert lib.ar_set_cost_model(0, 3, 1.0, 1.0) == binding.INVALID_ARGUMENT
     assert lib.ar_set_cost_model(0, 0, -1.0, 1.0) == binding.INVALID_ARGUMENT
     assert lib.ar_set_cost_model(0, 0, 1.0, 0.0) == binding.INVALID_ARGUMENT

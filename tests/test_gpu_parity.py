@@ -88,7 +88,14 @@ CALLS = {
                   lambda x, op, dt, root, **k: oracle.broadcast(x, root, dt, **k)),
     "tree_allreduce": (lambda b, op, root: ar.tree_allreduce(b, op=op),
                        lambda x, op, dt, root, **k: oracle.tree_allreduce(x, op, dt, **k)),
+    "reduce": (lambda b, op, root: ar.reduce(b, op=op, root=root),
+               lambda x, op, dt, root, **k: oracle.reduce(x, root, op, dt, **k)),
+    "scatter": (lambda b, op, root: ar.scatter(b, root=root),
+                lambda x, op, dt, root, **k: oracle.scatter(x, root, dt, **k)),
+    "gather": (lambda b, op, root: ar.gather(b, root=root),
+               lambda x, op, dt, root, **k: oracle.gather(x, root, dt, **k)),
 }
+NO_OP = ("allgather", "broadcast", "scatter", "gather")
 
 
 def compare_collective(coll, x, dtype, op, root, impls=IMPLS, check_counters=True):
@@ -156,7 +163,7 @@ def test_parity_elementwise(case, coll):
     name, n, t, dtype, dist, ops = case
     x = workloads.host_inputs(n, t, dtype, dist, seed=zlib.crc32(name.encode()) % 100_000, params=_params(dist, n))
     root = (n - 1) // 2 if n > 1 else 0
-    for op in (ops if coll not in ("allgather", "broadcast") else ("sum",)):
+    for op in (ops if coll not in NO_OP else ("sum",)):
         compare_collective(coll, x, dtype, op, root)
 
 
@@ -428,6 +435,28 @@ def test_zero_n64_reduce_scatter_then_allgather_and_broadcast():
     ar.set_impl("fused")
 
 
+def test_zero_n64_reduce_scatter_gather_full_size():
+    """N=64, T=16,777,217 float32 (ragged chunks): Reduce, Scatter and Gather
+    to a root in the middle, on sampled windows; the ranks that the pages say
+    keep their data are compared whole on the device."""
+    w = workloads.WORKLOADS["zero_n64"]
+    size = -(-w.count // w.nranks)
+    cuts = [c * size for c in range(1, w.nranks, 9)] + [63 * size]
+    root = 37
+    for coll, run in (("reduce", lambda b: ar.reduce(b, root=root)),
+                      ("scatter", lambda b: ar.scatter(b, root=root)),
+                      ("gather", lambda b: ar.gather(b, root=root))):
+        bufs = _device_inputs(w)
+        keep = {r: bufs[r].clone() for r in (0, 5, 63)}
+        check_windows(coll, bufs, run, w.dtype, root=root, cuts=cuts, seed=5,
+                      ranks=[0, 1, root, 62, 63])
+        if coll in ("reduce", "gather"):
+            for r, v in keep.items():
+                assert torch.equal(bufs[r], v), f"{coll} changed rank {r}"
+        del bufs, keep
+        torch.cuda.empty_cache()
+
+
 def test_rank_buffers_beyond_4_gib():
     """Two ranks of 2^30 + 3 float32 each (just over 4 GiB per buffer): byte
     offsets above 2^32 inside one buffer, with a ragged tail."""
@@ -465,7 +494,7 @@ def test_bfloat16_subnormals_ties_and_overflow():
 
 @pytest.mark.parametrize("impl", IMPLS)
 @pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce", "reduce_scatter",
-                                  "allgather", "broadcast"])
+                                  "allgather", "broadcast", "reduce", "scatter", "gather"])
 def test_graph_capture_replays_match_eager(coll, impl):
     """A collective captured into a HIP graph (kernel launches only; the
     library records no memset) replays correctly several times in a row, with

@@ -17,14 +17,17 @@ from .binding import (  # noqa: F401
     counters,
     expected_bytes,
     expected_steps,
+    gather,
     get_cost_model,
     get_impl,
     lib,
     predict_time,
     raw_call,
+    reduce,
     reduce_scatter,
     reset_counters,
     ring_allreduce,
+    scatter,
     set_cost_model,
     set_impl,
     tree_allreduce,

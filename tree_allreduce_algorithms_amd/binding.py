@@ -18,7 +18,7 @@ SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR = 0, 1, 2, 3
 DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 COLLECTIVES = {"ring_allreduce": 0, "reduce_scatter": 1, "allgather": 2, "broadcast": 3,
-               "tree_allreduce": 4}
+               "tree_allreduce": 4, "reduce": 5, "scatter": 6, "gather": 7}
 IMPLS = {"fused": 0, "step": 1}
 
 # name -> (restype, argtypes), in the order include/ar.h declares them
@@ -30,6 +30,9 @@ SIGNATURES = {
     "ar_allgather": (_I, [_PP, _I, _SZ, _I, _VP]),
     "ar_broadcast": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
     "ar_tree_allreduce": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_reduce": (_I, [_PP, _I, _SZ, _I, _I, _I, _VP]),
+    "ar_scatter": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_gather": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
     "ar_allreduce": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
     "ar_allreduce_choice": (_I, [_I, _SZ, _I, ctypes.POINTER(_I)]),
     "ar_predict_time": (_I, [_I, _I, _I, _SZ, _I, ctypes.POINTER(ctypes.c_double)]),
@@ -104,8 +107,10 @@ def raw_call(name, ptrs, count, dtype, op=None, root=None, stream=0):
         status = fn(pp, n, count, dt, OPS[op], stream)
     elif name == "allgather":
         status = fn(pp, n, count, dt, stream)
-    elif name == "broadcast":
+    elif name in ("broadcast", "scatter", "gather"):
         status = fn(pp, n, count, dt, root, stream)
+    elif name == "reduce":
+        status = fn(pp, n, count, dt, OPS[op], root, stream)
     else:
         raise ValueError(name)
     del keep
@@ -178,6 +183,21 @@ def broadcast(tensors, root=0, stream=None):
 def tree_allreduce(tensors, op="sum", stream=None):
     """Double-binary-tree AllReduce in place (see ar_tree_allreduce)."""
     return _collective("tree_allreduce", tensors, op=op, stream=stream)
+
+
+def reduce(tensors, op="sum", root=0, stream=None):
+    """Reduce in place into tensors[root]; the other tensors keep their data."""
+    return _collective("reduce", tensors, op=op, root=root, stream=stream)
+
+
+def scatter(tensors, root=0, stream=None):
+    """Scatter: chunk c of tensors[root] is copied into chunk c of tensors[c]."""
+    return _collective("scatter", tensors, root=root, stream=stream)
+
+
+def gather(tensors, root=0, stream=None):
+    """Gather: chunk c of tensors[c] is copied into chunk c of tensors[root]."""
+    return _collective("gather", tensors, root=root, stream=stream)
 
 
 def allreduce(tensors, op="sum", stream=None):

@@ -37,21 +37,25 @@ thread_local int t_last_hip_error = 0;
 // (1 KiB to 256 MiB per rank, Infinity Cache flushed before every call) on one
 // MI355X.  ReduceScatter, AllGather and Broadcast were measured at one size
 // (N=64, 64 MB per rank), which fixes their bandwidth; they take the
-// AllReduce fit's per-launch alpha.
+// AllReduce fit's per-launch alpha.  Reduce runs the tree fold kernel and
+// Scatter / Gather one copy step, so they take those kernels' coefficients.
 struct CostCoeff {
   double alpha_us;
   double gbps;
 };
 std::mutex g_cost_mu;
-CostCoeff g_cost[5][2] = {
+CostCoeff g_cost[8][2] = {
     {{6.18, 5905.0}, {3.16, 6186.0}},   // ring AllReduce: fused, step
     {{6.18, 5721.0}, {3.16, 5243.0}},   // ReduceScatter
     {{6.18, 4940.0}, {3.16, 4609.0}},   // AllGather
     {{6.18, 5052.0}, {3.16, 5790.0}},   // Broadcast
     {{6.21, 5825.0}, {3.24, 6090.0}},   // double-tree AllReduce
+    {{6.21, 5825.0}, {6.21, 5825.0}},   // Reduce (fused either way)
+    {{3.16, 5790.0}, {3.16, 5790.0}},   // Scatter (one step either way)
+    {{3.16, 5790.0}, {3.16, 5790.0}},   // Gather (one step either way)
 };
 
-bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_TREE_ALLREDUCE; }
+bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_GATHER; }
 bool impl_ok(int impl) { return impl == AR_IMPL_FUSED || impl == AR_IMPL_STEP; }
 
 double predict_us(ar_collective_t coll, ar_impl_t impl, int n, size_t count, ar_dtype_t dtype) {
@@ -111,7 +115,11 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
   const bool vec = aligned16;
 
   hipError_t err = hipSuccess;
-  if (impl == AR_IMPL_STEP) {
+  if (coll == AR_REDUCE) {
+    // one implementation: the partials of the rounds live in registers, so
+    // no rank other than the root is written
+    err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, root, vec, stream);
+  } else if (impl == AR_IMPL_STEP || coll == AR_SCATTER || coll == AR_GATHER) {
     for (const ar::Step& s : sched) {
       err = ar::launch_step(ptrs, s, dtype, aop, vec, stream);
       if (err != hipSuccess) break;
@@ -131,7 +139,9 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
         err = ar::launch_fanout(ptrs, n, count, dtype, true, root, vec, stream);
         break;
       case AR_TREE_ALLREDUCE:
-        err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, vec, stream);
+        err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, vec, stream);
+        break;
+      default:   // Reduce, Scatter and Gather are dispatched above
         break;
     }
   }
@@ -174,6 +184,24 @@ ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dt
                               ar_op_t op, void* stream) {
   if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_TREE_ALLREDUCE, bufs, nranks, count, dtype, static_cast<int>(op), -1, stream);
+}
+
+ar_status_t ar_reduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, ar_op_t op,
+                      int root, void* stream) {
+  if (!ar::op_ok(static_cast<int>(op)) || root < 0) return AR_ERROR_INVALID_ARGUMENT;
+  return run(AR_REDUCE, bufs, nranks, count, dtype, static_cast<int>(op), root, stream);
+}
+
+ar_status_t ar_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
+                       void* stream) {
+  if (root < 0) return AR_ERROR_INVALID_ARGUMENT;
+  return run(AR_SCATTER, bufs, nranks, count, dtype, -1, root, stream);
+}
+
+ar_status_t ar_gather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
+                      void* stream) {
+  if (root < 0) return AR_ERROR_INVALID_ARGUMENT;
+  return run(AR_GATHER, bufs, nranks, count, dtype, -1, root, stream);
 }
 
 ar_status_t ar_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, ar_op_t op,
@@ -238,10 +266,11 @@ ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar
   if (nranks < 1 || nranks > AR_MAX_RANKS || !ar::dtype_ok(static_cast<int>(dtype)) ||
       sent == nullptr || recv == nullptr || ar::expected_steps(coll, nranks) < 0)
     return AR_ERROR_INVALID_ARGUMENT;
-  if (coll == AR_BROADCAST && (root < 0 || root >= nranks)) return AR_ERROR_INVALID_ARGUMENT;
+  const bool rooted =
+      coll == AR_BROADCAST || coll == AR_REDUCE || coll == AR_SCATTER || coll == AR_GATHER;
+  if (rooted && (root < 0 || root >= nranks)) return AR_ERROR_INVALID_ARGUMENT;
   for (int r = 0; r < nranks; ++r) sent[r] = recv[r] = 0;
-  const std::vector<ar::Step> sched =
-      ar::schedule_for(coll, nranks, count, coll == AR_BROADCAST ? root : 0);
+  const std::vector<ar::Step> sched = ar::schedule_for(coll, nranks, count, rooted ? root : 0);
   ar::count_bytes(sched, ar::itemsize(dtype), sent, recv);
   return AR_SUCCESS;
 }

@@ -30,10 +30,12 @@ hipError_t launch_ring_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtyp
 hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
                          bool from_root, int root, bool vec, hipStream_t stream);
 
-// Fused double binomial tree: per element, the pairwise fold of the tree that
-// owns it, stored into every rank.
+// Fused binomial tree fold.  root < 0: the double tree, per element the
+// pairwise fold of the tree that owns it, stored into every rank.  root >= 0:
+// Reduce, one tree over the whole buffer on roles (rank - root) mod N, stored
+// into bufs[root] only.
 hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                            ar_op_t op, bool vec, hipStream_t stream);
+                            ar_op_t op, int root, bool vec, hipStream_t stream);
 
 // One schedule step: all of its transfers in one launch.
 hipError_t launch_step(const RankPtrs& ptrs, const Step& step, ar_dtype_t dtype, ar_op_t op,

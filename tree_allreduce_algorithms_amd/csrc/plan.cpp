@@ -110,6 +110,37 @@ std::vector<Step> broadcast_schedule(int n, uint64_t count, int root) {
   return out;
 }
 
+// Reduce to `root`: the binomial reduce rounds on roles (rank - root) mod N
+// over the whole buffer.  The fused kernel evaluates these rounds in
+// registers; the schedule gives the counters.
+std::vector<Step> reduce_schedule(int n, uint64_t count, int root) {
+  std::vector<Step> out;
+  for (int k = 0; k < tree_depth(n); ++k) {
+    const int stride = 1 << k;
+    Step s{true, {}};
+    for (int q = 0; q + stride < n; q += 2 * stride)
+      s.xfers.push_back({(q + stride + root) % n, (q + root) % n, 0, count});
+    out.push_back(std::move(s));
+  }
+  return out;
+}
+
+// Scatter / Gather: one step of direct transfers of chunk c between the root
+// and rank c.
+std::vector<Step> scatter_schedule(int n, uint64_t count, int root, bool to_root) {
+  std::vector<Step> out;
+  if (n < 2) return out;
+  Step s{false, {}};
+  for (int c = 0; c < n; ++c) {
+    if (c == root) continue;
+    uint64_t lo, hi;
+    chunk_bounds(n, count, c, &lo, &hi);
+    s.xfers.push_back(to_root ? Transfer{c, root, lo, hi} : Transfer{root, c, lo, hi});
+  }
+  out.push_back(std::move(s));
+  return out;
+}
+
 std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int root) {
   switch (coll) {
     case AR_RING_ALLREDUCE: {
@@ -122,6 +153,9 @@ std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int 
     case AR_ALLGATHER: return ring_allgather_schedule(n, count);
     case AR_BROADCAST: return broadcast_schedule(n, count, root);
     case AR_TREE_ALLREDUCE: return tree_allreduce_schedule(n, count);
+    case AR_REDUCE: return reduce_schedule(n, count, root);
+    case AR_SCATTER: return scatter_schedule(n, count, root, false);
+    case AR_GATHER: return scatter_schedule(n, count, root, true);
   }
   return {};
 }
@@ -141,29 +175,36 @@ int expected_steps(ar_collective_t coll, int n) {
     case AR_RING_ALLREDUCE: return 2 * (n - 1);
     case AR_REDUCE_SCATTER:
     case AR_ALLGATHER: return n - 1;
-    case AR_BROADCAST: return tree_depth(n);
+    case AR_BROADCAST:
+    case AR_REDUCE: return tree_depth(n);
     case AR_TREE_ALLREDUCE: return 2 * tree_depth(n);
+    case AR_SCATTER:
+    case AR_GATHER: return n > 1 ? 1 : 0;
   }
   return -1;
 }
 
 int impl_launches(ar_collective_t coll, ar_impl_t impl, int n) {
-  if (impl == AR_IMPL_FUSED) return n > 1 ? 1 : 0;
+  // Reduce has one (fused) implementation; Scatter and Gather are one step.
+  if (impl == AR_IMPL_FUSED || coll == AR_REDUCE) return n > 1 ? 1 : 0;
   return expected_steps(coll, n);
 }
 
 uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz) {
   if (n <= 1) return 0;
   const uint64_t un = static_cast<uint64_t>(n);
-  if (impl == AR_IMPL_FUSED) {
+  // Scatter and Gather run their one schedule step under either
+  // implementation (modelled with the root at rank 0); Reduce runs fused
+  // under either.
+  const bool fused = impl == AR_IMPL_FUSED || coll == AR_REDUCE;
+  if (fused && coll != AR_SCATTER && coll != AR_GATHER) {
     switch (coll) {
       case AR_RING_ALLREDUCE:
       case AR_TREE_ALLREDUCE: return 2 * un * count * isz;
-      case AR_REDUCE_SCATTER: return (un + 1) * count * isz;
-      case AR_ALLGATHER:
-      case AR_BROADCAST: return un * count * isz;
+      case AR_REDUCE_SCATTER:
+      case AR_REDUCE: return (un + 1) * count * isz;
+      default: return un * count * isz;   // AllGather, Broadcast
     }
-    return 0;
   }
   uint64_t bytes = 0;
   for (const Step& s : schedule_for(coll, n, count, 0))

@@ -48,6 +48,8 @@ std::vector<Step> ring_reduce_scatter_schedule(int n, uint64_t count);
 std::vector<Step> ring_allgather_schedule(int n, uint64_t count);
 std::vector<Step> tree_allreduce_schedule(int n, uint64_t count);
 std::vector<Step> broadcast_schedule(int n, uint64_t count, int root);
+std::vector<Step> reduce_schedule(int n, uint64_t count, int root);
+std::vector<Step> scatter_schedule(int n, uint64_t count, int root, bool to_root);
 std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int root);
 
 // Adds the bytes of every transfer to sent[src] / recv[dst].

@@ -1,4 +1,5 @@
-// Fused double binomial tree AllReduce (gfx950).
+// Fused binomial-tree folds (gfx950): the double-tree AllReduce and the
+// Reduce to one root.
 #include "device_common.hpp"
 
 namespace ar {
@@ -28,6 +29,7 @@ struct TreeArgs {
   uint64_t half;
   uint64_t tiles;
   int n;
+  int root;   // >= 0: Reduce to `root` (one tree over the whole buffer)
 };
 
 constexpr int kTreeUnroll = 2;
@@ -35,10 +37,12 @@ constexpr int kTreeBatch = 8;
 
 constexpr int ilog2_ceil(int v) { return v <= 1 ? 0 : 1 + ilog2_ceil((v + 1) / 2); }
 
-// Folds U packs (pack index idx[u], valid where live[u]) of every role of one
-// tree; LOAD(rank, u) loads rank's pack u.
+// Folds U packs of every role of one tree; load(rank, u) loads rank's pack u.
+// Roles map to ranks as role == rank (tree 0), N-1-role (tree 1) or, for a
+// Reduce, (role + root) mod N.
 template <ar_dtype_t DT, ar_op_t OP, int NMAX, int U, class P, class Load>
-__device__ __forceinline__ void tree_fold_values(int n, int tree, const Load& load, P out[U]) {
+__device__ __forceinline__ void tree_fold_values(int n, int tree, int root, const Load& load,
+                                                 P out[U]) {
   constexpr int L = ilog2_ceil(NMAX) + 1;
   P slot[L][U];
 #pragma unroll
@@ -49,7 +53,7 @@ __device__ __forceinline__ void tree_fold_values(int n, int tree, const Load& lo
     for (int j = 0; j < kTreeBatch; ++j) {
       const int q = q0 + j;
       if (q < n) {
-        const int rank = tree == 0 ? q : n - 1 - q;
+        const int rank = root >= 0 ? wrap_rank(q + root, n) : (tree == 0 ? q : n - 1 - q);
 #pragma unroll
         for (int u = 0; u < U; ++u) in[j][u] = load(rank, u);
       }
@@ -99,8 +103,9 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
 
   const int n = a.n;
   const int tree = blockIdx.y;
-  const uint64_t lo = tree == 0 ? 0 : a.half;
-  const uint64_t hi = tree == 0 ? a.half : a.count;
+  const int root = a.root;
+  const uint64_t lo = (root >= 0 || tree == 0) ? 0 : a.half;
+  const uint64_t hi = (root >= 0 || tree != 0) ? a.count : a.half;
   if (lo >= hi) return;
   const Span s = make_span<K>(lo, hi);
 
@@ -111,12 +116,12 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
     const TileLanes<U, sizeof(P)> ln(tp, s.plo, s.phi);
     P v[U];
     tree_fold_values<DT, OP, NMAX, U, P>(
-        n, tree,
+        n, tree, root,
         [&](int rank, int u) {
           return ln.live[u] ? load_stream<P>(at(a.ptrs.p[rank], toff), ln.off[u]) : P{};
         },
         v);
-    for (int r = 0; r < n; ++r) {
+    for (int r = root >= 0 ? root : 0; r < (root >= 0 ? root + 1 : n); ++r) {
       char* dst = at(a.ptrs.p[r], toff);
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -128,8 +133,9 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
     const uint64_t e = s.scalar_index(threadIdx.x);
     S v[1];
     tree_fold_values<DT, OP, NMAX, 1, S>(
-        n, tree, [&](int rank, int) { return load<S>(a.ptrs.p[rank], e); }, v);
-    for (int r = 0; r < n; ++r) store<S>(a.ptrs.p[r], e, v[0]);
+        n, tree, root, [&](int rank, int) { return load<S>(a.ptrs.p[rank], e); }, v);
+    for (int r = root >= 0 ? root : 0; r < (root >= 0 ? root + 1 : n); ++r)
+      store<S>(a.ptrs.p[r], e, v[0]);
   }
 }
 
@@ -145,8 +151,10 @@ template <ar_dtype_t DT, ar_op_t OP>
 hipError_t tree_fold_typed(const TreeArgs& a, bool vec, hipStream_t stream) {
   constexpr int K = 16 / sizeof(typename Elem<DT>::T);
   TreeArgs b = a;
-  b.tiles = tiles_for(a.half, vec ? K : 1, kTreeUnroll);   // tree 0's half is never the shorter
-  const dim3 grid(grid_x(b.tiles), 2);
+  // Reduce: one segment, the whole buffer; double tree: tree 0's half, never
+  // the shorter one, bounds both segments.
+  b.tiles = tiles_for(a.root >= 0 ? a.count : a.half, vec ? K : 1, kTreeUnroll);
+  const dim3 grid(grid_x(b.tiles), a.root >= 0 ? 1 : 2);
   return launch(vec ? tree_fold_fn<DT, OP, true>(a.n) : tree_fold_fn<DT, OP, false>(a.n), grid, b,
                 stream);
 }
@@ -154,13 +162,14 @@ hipError_t tree_fold_typed(const TreeArgs& a, bool vec, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                            ar_op_t op, bool vec, hipStream_t stream) {
+                            ar_op_t op, int root, bool vec, hipStream_t stream) {
   TreeArgs a;
   a.ptrs = ptrs;
   a.count = count;
   a.half = tree_split(count);
   a.n = n;
   a.tiles = 0;
+  a.root = root;
   AR_DISPATCH(tree_fold_typed, dtype, op, a, vec, stream);
 }
 
