@@ -23,7 +23,8 @@ Sources (cited by page title and section):
 * "从零实现集合通信" (Collectives from scratch), section "两趟实现 ring
   allreduce" (two-pass ring) and its per-primitive cost table.
 * Lecture 09 sections 3.2-3.4 for Scatter, Gather and Reduce (each rank not
-  named as receiving keeps its data).
+  named as receiving keeps its data), section 3.8 and lab 4 (section 7.4)
+  for AllToAll.
 
 Pins (what the oracle is checked against in ``tests/test_oracle_*.py``):
 int32 brute force, hand-derived order-revealing fp32 examples, the worked
@@ -46,6 +47,7 @@ from .numerics import (  # noqa: F401
 )
 from .collectives import (  # noqa: F401
     Result,
+    alltoall,
     broadcast,
     ceil_log2,
     chunk_layout,

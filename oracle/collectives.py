@@ -344,3 +344,33 @@ def gather(x, root, dtype, window_start=0, total=None):
         bufs[root][span[c]] = payload
         _count(sent, recv, c, root, payload.size, dtype)
     return Result(bufs, sent, recv, 1 if n > 1 else 0)
+
+
+# --- AllToAll ---------------------------------------------------------------------
+
+def alltoall_slot(src, dst):
+    """Block of rank ``dst`` that receives rank ``src``'s block ``dst``: block
+    ``src`` (the cross-rank transpose, recv[dst][src] = send[src][dst], of
+    Lecture 09 section 3.8 and lab 4 in section 7.4)."""
+    return src
+
+
+def alltoall(x, dtype):
+    """AllToAll (Lecture 09, section 3.8; lab 4, section 7.4): every rank's
+    buffer is N equal blocks of T/N elements; block j of rank i is meant for
+    rank j, which receives it in block i.  One step: every rank first copies
+    out the N-1 blocks it sends (the snapshot), then every block is
+    delivered; a rank's own block (j == i) stays in place.  N must divide T.
+    Whole buffers only: an output element comes from another position of
+    another rank, so the windowed mode of the other functions does not apply.
+    """
+    n, length, total, bufs, sent, recv = _setup(x, dtype, 0, None)
+    if length % n:
+        raise ValueError("AllToAll needs N to divide T")
+    size = length // n
+    block = lambda b: slice(b * size, (b + 1) * size)
+    packets = [(i, j, bufs[i][block(j)].copy()) for i in range(n) for j in range(n) if i != j]
+    for i, j, payload in packets:
+        bufs[j][block(alltoall_slot(i, j))] = payload
+        _count(sent, recv, i, j, payload.size, dtype)
+    return Result(bufs, sent, recv, 1 if n > 1 else 0)

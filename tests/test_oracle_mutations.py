@@ -23,7 +23,7 @@ def _ints(n, t, seed):
 def _pins_hold():
     """A compact run of the pins: int32 brute force for AllReduce, ownership
     after ReduceScatter, AllGather, ragged byte counts, the order goldens."""
-    for n, t in [(4, 1024), (5, 23), (8, 1000), (3, 7)]:
+    for n, t in [(4, 1024), (5, 23), (8, 1000), (3, 7), (4, 12)]:
         x = _ints(n, t, n + t)
         want = (np.stack(x).astype(np.int64).sum(axis=0) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
         ar = oracle.ring_allreduce(x, "sum", "int32")
@@ -44,6 +44,11 @@ def _pins_hold():
         red = oracle.reduce(x, root, "sum", "int32")
         if not np.array_equal(red.bufs[root], want) or int(red.sent[root]) != 0:
             return False
+        if t % n == 0:
+            a2a = oracle.alltoall(x, "int32")
+            b = t // n
+            if not np.array_equal(a2a.bufs[1][:b], x[0][b:2 * b]):
+                return False
         bc = oracle.broadcast(x, root, "int32")
         if any(not np.array_equal(b, x[root]) for b in bc.bufs) or int(bc.recv[root]) != 0:
             return False
@@ -70,6 +75,7 @@ MUTATIONS = {
     "ring_turns_left": ("ring_next", lambda r, n: (r - 1) % n),
     "tree_one_not_mirrored": ("tree_rank", lambda tree, role, n: role),
     "rooted_tree_ignores_root": ("rooted_rank", lambda role, root, n: role),
+    "alltoall_keeps_block_index": ("alltoall_slot", lambda src, dst: dst),
     "receiver_overwrites_instead_of_adding": (
         "combine", lambda local, incoming, op, dtype: np.array(incoming, copy=True)),
     "receiver_drops_incoming": ("combine", lambda local, incoming, op, dtype: np.array(local, copy=True)),
