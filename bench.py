@@ -56,7 +56,7 @@ HBM_PEAK_GBPS = 8000.0
 DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
 MAX_CALLS = 35
 COLLECTIVES = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce",
-               "allreduce", "reduce", "scatter", "gather"]
+               "allreduce", "reduce", "scatter", "gather", "alltoall"]
 KERNEL = {  # collective, impl -> kernel that dominates one call
     ("ring_allreduce", "fused"): "ring_fold_kernel",
     ("reduce_scatter", "fused"): "ring_fold_kernel",
@@ -65,6 +65,8 @@ KERNEL = {  # collective, impl -> kernel that dominates one call
     ("tree_allreduce", "fused"): "tree_fold_kernel",
     ("reduce", "fused"): "tree_fold_kernel",
     ("reduce", "step"): "tree_fold_kernel",   # Reduce has one (fused) implementation
+    ("alltoall", "fused"): "alltoall_kernel",
+    ("alltoall", "step"): "alltoall_kernel",
 }
 
 
@@ -129,6 +131,7 @@ def algorithmic_bytes(collective, n, t, isz):
         # one chunk per non-root rank, read once and written once
         "scatter": 2 * (t - -(-t // n)) * isz if n > 1 else 0,
         "gather": 2 * (t - -(-t // n)) * isz if n > 1 else 0,
+        "alltoall": 2 * (n - 1) * t * isz,     # every off-diagonal block read and written once
     }[collective]
 
 
@@ -139,7 +142,7 @@ def step_bytes(collective, n, t, isz):
     sent, _ = ar.expected_bytes(collective, n, t, "bfloat16" if isz == 2 else "int32")
     moved = sum(sent) // isz                     # elements transferred over all steps
     # share of those elements moved by reduce (rather than copy) transfers
-    if collective == "reduce":                   # one (fused) implementation
+    if collective in ("reduce", "alltoall"):     # one implementation
         return algorithmic_bytes(collective, n, t, isz)
     reduce_share = {"ring_allreduce": (1, 2), "tree_allreduce": (1, 2),
                     "reduce_scatter": (1, 1)}.get(collective, (0, 1))
@@ -173,7 +176,10 @@ def run_checker(collective, pristine, got, w, root, window):
         "reduce": lambda x, a: oracle.reduce(x, root, "sum", w.dtype, a, t),
         "scatter": lambda x, a: oracle.scatter(x, root, w.dtype, a, t),
         "gather": lambda x, a: oracle.gather(x, root, w.dtype, a, t),
+        "alltoall": lambda x, a: oracle.alltoall(x, w.dtype),
     }[collective]
+    if collective == "alltoall":
+        window = t   # an output element comes from another position: whole buffers
     secs, compared, bad = 0.0, 0, 0
     for a in range(0, t, window):
         b = min(t, a + window)
@@ -227,6 +233,7 @@ def run_one(args):
         "reduce": lambda b: ar.reduce(b, root=args.root),
         "scatter": lambda b: ar.scatter(b, root=args.root),
         "gather": lambda b: ar.gather(b, root=args.root),
+        "alltoall": lambda b: ar.alltoall(b),
     }[args.collective]
     stream = torch.cuda.current_stream(dev)
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_mall else None
@@ -259,7 +266,7 @@ def run_one(args):
     launch_ms = sum(event_ms) / len(event_ms)
     per_call_s = (launch_ms * 1e-3) if args.flush_mall else wall / args.steps
     alg = algorithmic_bytes(ran, n, t, isz)
-    launches = (1 if args.impl == "fused" or ran == "reduce"
+    launches = (1 if args.impl == "fused" or ran in ("reduce", "alltoall")
                 else ar.expected_steps(ran, n))
     moved = alg if args.impl == "fused" else step_bytes(ran, n, t, isz)
     achieved = moved / (launch_ms * 1e-3) / 1e9
@@ -371,6 +378,7 @@ SUITE = [
     ("zero_n64", "scatter", "fused", []),
     ("zero_n64", "gather", "fused", []),
     ("large_grad_fp32", "reduce", "fused", []),
+    ("moe_alltoall", "alltoall", "fused", []),
     ("small_int32", "ring_allreduce", "fused", ["--steps", "30"]),
     ("small_int32", "reduce_scatter", "fused", ["--steps", "30"]),
     ("small_int32", "allgather", "fused", ["--steps", "30"]),

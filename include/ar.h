@@ -59,7 +59,8 @@
  *               is kept for ar_last_hip_error().  (Faults during execution
  *               surface at the caller's next synchronisation.)
  *         count == 0 or nranks == 1 is a valid no-op (AR_SUCCESS, nothing
- *         enqueued).
+ *         enqueued); with count == 0 the entries of bufs are not inspected
+ *         (an empty tensor may have a NULL data pointer).
  * Counters every successful call adds the logical inter-rank bytes of its
  *         schedule (each transfer of k elements adds k * element size to the
  *         sender's `sent` and the receiver's `recv`) and its schedule steps
@@ -98,7 +99,8 @@ typedef enum {
   AR_TREE_ALLREDUCE = 4,
   AR_REDUCE = 5,
   AR_SCATTER = 6,
-  AR_GATHER = 7
+  AR_GATHER = 7,
+  AR_ALLTOALL = 8
 } ar_collective_t;
 
 /* How a collective is executed; results are bit-identical either way.
@@ -176,6 +178,16 @@ ar_status_t ar_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t d
 ar_status_t ar_gather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
                       void* stream);
 
+/* AllToAll [L09 3.8, lab 4 in 7.4]: every buffer is N equal blocks of
+ * count/N elements; block j of bufs[i] is meant for rank j, which receives
+ * it in block i (recv[j][i] = send[i][j], a transpose across ranks).  Block
+ * i of bufs[i] stays in place.  count must be a multiple of nranks
+ * (otherwise AR_ERROR_INVALID_ARGUMENT).  One step: each rank sends and
+ * receives (N-1) blocks.  One kernel swaps block j of rank i with block i of
+ * rank j for every pair i < j, under either implementation. */
+ar_status_t ar_alltoall(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                        void* stream);
+
 /* ---- size-based choice between ring and tree ----------------------------- */
 
 /* AllReduce that picks the ring or the double tree by message size [L09 5.3:
@@ -222,14 +234,15 @@ ar_status_t ar_chunk_range(int nranks, size_t count, int chunk, size_t* begin, s
 /* Logical bytes each rank sends and receives in one call of `coll` with these
  * arguments ([SCR cost table]; e.g. 2T(N-1)/N per rank for the ring when N
  * divides T).  sent and recv are caller arrays of nranks uint64_t.  `root`
- * is used for AR_BROADCAST, AR_REDUCE, AR_SCATTER and AR_GATHER only. */
+ * is used for AR_BROADCAST, AR_REDUCE, AR_SCATTER and AR_GATHER only;
+ * AR_ALLTOALL needs count to be a multiple of nranks. */
 ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype,
                               int root, uint64_t* sent, uint64_t* recv);
 
 /* Schedule steps of one call: 2(N-1) ring AllReduce, N-1 ReduceScatter and
  * AllGather, ceil(log2 N) Broadcast and Reduce, 2 ceil(log2 N) tree
- * AllReduce, 1 Scatter and Gather (0 for every collective when N == 1); -1
- * on a bad argument. */
+ * AllReduce, 1 Scatter, Gather and AllToAll (0 for every collective when
+ * N == 1); -1 on a bad argument. */
 int ar_expected_steps(ar_collective_t coll, int nranks);
 
 /* Process-wide cumulative counters since load or the last reset.  Copies the

@@ -68,6 +68,7 @@ ORACLE_CALLS = {
     "reduce": lambda x, root: oracle.reduce(x, root, "sum", "int32"),
     "scatter": lambda x, root: oracle.scatter(x, root, "int32"),
     "gather": lambda x, root: oracle.gather(x, root, "int32"),
+    "alltoall": lambda x, root: oracle.alltoall(x, "int32"),
 }
 
 
@@ -77,6 +78,10 @@ ORACLE_CALLS = {
 @pytest.mark.parametrize("dtype", ["int32", "bfloat16"])
 def test_expected_bytes_and_steps_match_oracle(coll, n, t, dtype):
     root = (n - 1) // 2
+    if coll == "alltoall" and t % n:
+        with pytest.raises(ar.ArError):
+            ar.expected_bytes(coll, n, t, dtype)
+        return
     x = [np.zeros(t, np.int32) for _ in range(n)]
     res = ORACLE_CALLS[coll](x, root)
     scale = 2 if dtype == "bfloat16" else 4
@@ -110,7 +115,7 @@ def _fake(n, stride=1 << 20, offset=0):
 
 
 ALL = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce", "reduce",
-       "scatter", "gather"]
+       "scatter", "gather", "alltoall"]
 ROOTED = ("broadcast", "reduce", "scatter", "gather")
 
 
@@ -136,6 +141,8 @@ def test_invalid_arguments(name):
         fn = getattr(lib, "ar_" + name)
         assert fn(pp, 4, 16, 1, 4, None) == inv                     # root out of range
         assert fn(pp, 4, 16, 1, -1, None) == inv
+    if name == "alltoall":
+        assert lib.ar_alltoall(pp, 4, 18, 1, None) == inv           # 4 does not divide 18
     if name == "reduce":
         assert lib.ar_reduce(pp, 4, 16, 1, 0, 4, None) == inv       # root out of range
         assert lib.ar_reduce(pp, 4, 16, 1, 0, -1, None) == inv
@@ -204,6 +211,8 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
         return 0
     if coll == "reduce":                 # one fused implementation
         return (n + 1) * t * s
+    if coll == "alltoall":               # every off-diagonal block read and written once
+        return 2 * n * (n - 1) * (t // n) * s
     if impl == "fused" and coll not in ("scatter", "gather"):
         return {"ring_allreduce": 2 * n * t, "tree_allreduce": 2 * n * t,
                 "reduce_scatter": (n + 1) * t, "allgather": n * t, "broadcast": n * t}[coll] * s
@@ -220,7 +229,7 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
                                        (64, 1_000_003, "float32"), (2, 7, "int32")])
 def test_predicted_time_is_the_documented_formula(coll, impl, n, t, dtype):
     alpha, gbps = ar.get_cost_model(coll, impl)
-    launches = 1 if impl == "fused" or coll == "reduce" else ar.expected_steps(coll, n)
+    launches = 1 if impl == "fused" or coll in ("reduce", "alltoall") else ar.expected_steps(coll, n)
     if n == 1:
         launches = 0
     want = launches * alpha + _oracle_hbm_bytes(coll, impl, n, t, dtype) / (gbps * 1e3)
@@ -262,7 +271,7 @@ def test_allreduce_choice_switches_at_the_model_crossover():
 
 def test_cost_model_arguments_are_validated():
     lib = ar.lib()
-    assert lib.ar_set_cost_model(8, 0, 1.0, 1.0) == binding.INVALID_ARGUMENT
+    assert lib.ar_set_cost_model(9, 0, 1.0, 1.0) == binding.INVALID_ARGUMENT
     assert lib.ar_set_cost_model(0, 3, 1.0, 1.0) == binding.INVALID_ARGUMENT
     assert lib.ar_set_cost_model(0, 0, -1.0, 1.0) == binding.INVALID_ARGUMENT
     assert lib.ar_set_cost_model(0, 0, 1.0, 0.0) == binding.INVALID_ARGUMENT
@@ -276,6 +285,7 @@ def test_cost_model_arguments_are_validated():
     assert _call("allreduce", _fake(65)) == binding.INVALID_ARGUMENT
     assert _call("allreduce", _fake(4, offset=2)) == binding.INVALID_ARGUMENT
     assert _call("allreduce", _fake(4), count=0) == binding.SUCCESS
+    assert _call("ring_allreduce", [0, 0, 0], count=0) == binding.SUCCESS   # empty tensors
 
 
 def test_costfit_recovers_known_coefficients():

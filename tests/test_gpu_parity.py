@@ -94,13 +94,24 @@ CALLS = {
                 lambda x, op, dt, root, **k: oracle.scatter(x, root, dt, **k)),
     "gather": (lambda b, op, root: ar.gather(b, root=root),
                lambda x, op, dt, root, **k: oracle.gather(x, root, dt, **k)),
+    "alltoall": (lambda b, op, root: ar.alltoall(b),
+                 lambda x, op, dt, root, **k: oracle.alltoall(x, dt)),
 }
-NO_OP = ("allgather", "broadcast", "scatter", "gather")
+NO_OP = ("allgather", "broadcast", "scatter", "gather", "alltoall")
+
+
+def fit_inputs(coll, x):
+    """AllToAll needs N to divide T: cut every rank to the largest multiple."""
+    if coll != "alltoall":
+        return x
+    n, t = len(x), len(x[0])
+    return [a[: t - t % n].copy() for a in x]
 
 
 def compare_collective(coll, x, dtype, op, root, impls=IMPLS, check_counters=True):
     """Run `coll` on device copies of x with each implementation; compare every
     element the collective defines (owned chunks only for ReduceScatter)."""
+    x = fit_inputs(coll, x)
     n, t = len(x), len(x[0])
     want = CALLS[coll][1](x, op, dtype, root).bufs
     owned = oracle.chunk_layout(n, t)
@@ -273,12 +284,14 @@ def test_element_aligned_buffers_match_oracle(dtype, layout):
     """Buffers aligned only to the element size take the element-at-a-time
     path; its results must equal the oracle bit for bit, for every collective
     and both implementations, without touching memory outside the views."""
-    n, t = 5, 10_007
+    n, t0 = 5, 10_007
     offsets = [1] * n if layout == "all_offset" else [r % 3 for r in range(n)]
     dist = "int_uniform" if dtype == "int32" else "normal"
-    x = workloads.host_inputs(n, t, dtype, dist, 51, _params(dist, n))
-    owned = oracle.chunk_layout(n, t)
+    x0 = workloads.host_inputs(n, t0, dtype, dist, 51, _params(dist, n))
     for coll in sorted(CALLS):
+        x = fit_inputs(coll, x0)
+        t = len(x[0])
+        owned = oracle.chunk_layout(n, t)
         want = CALLS[coll][1](x, "sum", dtype, 1).bufs
         for impl in IMPLS:
             announce(f"element-aligned {coll} impl={impl} dtype={dtype} layout={layout}")
@@ -494,13 +507,15 @@ def test_bfloat16_subnormals_ties_and_overflow():
 
 @pytest.mark.parametrize("impl", IMPLS)
 @pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce", "reduce_scatter",
-                                  "allgather", "broadcast", "reduce", "scatter", "gather"])
+                                  "allgather", "broadcast", "reduce", "scatter", "gather",
+                                  "alltoall"])
 def test_graph_capture_replays_match_eager(coll, impl):
     """A collective captured into a HIP graph (kernel launches only; the
     library records no memset) replays correctly several times in a row, with
     eager work and synchronisations between the replays."""
-    n, t = 8, 100_003
-    x = workloads.host_inputs(n, t, "float32", "normal", 61, {"std": 1.0})
+    n = 8
+    x = fit_inputs(coll, workloads.host_inputs(n, 100_003, "float32", "normal", 61, {"std": 1.0}))
+    t = len(x[0])
     want = CALLS[coll][1](x, "sum", "float32", 2).bufs
     owned = oracle.chunk_layout(n, t)
     ar.set_impl(impl)
@@ -560,3 +575,20 @@ def test_allreduce_runs_the_chosen_algorithm(impl):
         for c, (a, g) in saved.items():
             ar.set_cost_model(c, impl, a, g)
         ar.set_impl("fused")
+
+
+def test_alltoall_block_sizes_and_involution():
+    """AllToAll on block sizes that are and are not a multiple of 16 bytes
+    (16-byte packs vs one element at a time), bfloat16 and int32, N up to 64;
+    applying it twice restores the inputs."""
+    for n, b, dtype in ((4, 1, "int32"), (8, 4096, "float32"), (8, 4097, "float32"),
+                        (64, 520, "bfloat16"), (3, 1000, "bfloat16"), (16, 33, "int32")):
+        dist = "int_uniform" if dtype == "int32" else "normal"
+        x = workloads.host_inputs(n, n * b, dtype, dist, 91 + n, _params(dist, n))
+        compare_collective("alltoall", x, dtype, "sum", 0)
+        bufs = to_dev(x, dtype)
+        ar.alltoall(bufs)
+        ar.alltoall(bufs)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_same(to_host(bufs[r], dtype), x[r], dtype, f"involution n={n} b={b} rank {r}")

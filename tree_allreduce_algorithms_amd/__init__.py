@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     allgather,
     allreduce,
     allreduce_choice,
+    alltoall,
     broadcast,
     chunk_range,
     chunk_size,

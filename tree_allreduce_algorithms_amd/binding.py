@@ -18,7 +18,7 @@ SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR = 0, 1, 2, 3
 DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 COLLECTIVES = {"ring_allreduce": 0, "reduce_scatter": 1, "allgather": 2, "broadcast": 3,
-               "tree_allreduce": 4, "reduce": 5, "scatter": 6, "gather": 7}
+               "tree_allreduce": 4, "reduce": 5, "scatter": 6, "gather": 7, "alltoall": 8}
 IMPLS = {"fused": 0, "step": 1}
 
 # name -> (restype, argtypes), in the order include/ar.h declares them
@@ -33,6 +33,7 @@ SIGNATURES = {
     "ar_reduce": (_I, [_PP, _I, _SZ, _I, _I, _I, _VP]),
     "ar_scatter": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
     "ar_gather": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
+    "ar_alltoall": (_I, [_PP, _I, _SZ, _I, _VP]),
     "ar_allreduce": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
     "ar_allreduce_choice": (_I, [_I, _SZ, _I, ctypes.POINTER(_I)]),
     "ar_predict_time": (_I, [_I, _I, _I, _SZ, _I, ctypes.POINTER(ctypes.c_double)]),
@@ -105,7 +106,7 @@ def raw_call(name, ptrs, count, dtype, op=None, root=None, stream=0):
     dt = DTYPES[dtype]
     if name in ("ring_allreduce", "reduce_scatter", "tree_allreduce", "allreduce"):
         status = fn(pp, n, count, dt, OPS[op], stream)
-    elif name == "allgather":
+    elif name in ("allgather", "alltoall"):
         status = fn(pp, n, count, dt, stream)
     elif name in ("broadcast", "scatter", "gather"):
         status = fn(pp, n, count, dt, root, stream)
@@ -198,6 +199,11 @@ def scatter(tensors, root=0, stream=None):
 def gather(tensors, root=0, stream=None):
     """Gather: chunk c of tensors[c] is copied into chunk c of tensors[root]."""
     return _collective("gather", tensors, root=root, stream=stream)
+
+
+def alltoall(tensors, stream=None):
+    """AllToAll in place: block j of tensors[i] <-> block i of tensors[j]."""
+    return _collective("alltoall", tensors, stream=stream)
 
 
 def allreduce(tensors, op="sum", stream=None):

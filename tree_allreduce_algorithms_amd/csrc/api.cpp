@@ -44,7 +44,7 @@ struct CostCoeff {
   double gbps;
 };
 std::mutex g_cost_mu;
-CostCoeff g_cost[8][2] = {
+CostCoeff g_cost[9][2] = {
     {{6.18, 5905.0}, {3.16, 6186.0}},   // ring AllReduce: fused, step
     {{6.18, 5721.0}, {3.16, 5243.0}},   // ReduceScatter
     {{6.18, 4940.0}, {3.16, 4609.0}},   // AllGather
@@ -53,9 +53,10 @@ CostCoeff g_cost[8][2] = {
     {{6.21, 5825.0}, {6.21, 5825.0}},   // Reduce (fused either way)
     {{3.16, 5790.0}, {3.16, 5790.0}},   // Scatter (one step either way)
     {{3.16, 5790.0}, {3.16, 5790.0}},   // Gather (one step either way)
+    {{3.16, 5790.0}, {3.16, 5790.0}},   // AllToAll (one kernel either way)
 };
 
-bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_GATHER; }
+bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_ALLTOALL; }
 bool impl_ok(int impl) { return impl == AR_IMPL_FUSED || impl == AR_IMPL_STEP; }
 
 double predict_us(ar_collective_t coll, ar_impl_t impl, int n, size_t count, ar_dtype_t dtype) {
@@ -119,6 +120,8 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
     // one implementation: the partials of the rounds live in registers, so
     // no rank other than the root is written
     err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, root, vec, stream);
+  } else if (coll == AR_ALLTOALL) {
+    err = ar::launch_alltoall(ptrs, n, count, dtype, vec, stream);
   } else if (impl == AR_IMPL_STEP || coll == AR_SCATTER || coll == AR_GATHER) {
     for (const ar::Step& s : sched) {
       err = ar::launch_step(ptrs, s, dtype, aop, vec, stream);
@@ -141,7 +144,7 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
       case AR_TREE_ALLREDUCE:
         err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, vec, stream);
         break;
-      default:   // Reduce, Scatter and Gather are dispatched above
+      default:   // Reduce, Scatter, Gather and AllToAll are dispatched above
         break;
     }
   }
@@ -202,6 +205,13 @@ ar_status_t ar_gather(void* const* bufs, int nranks, size_t count, ar_dtype_t dt
                       void* stream) {
   if (root < 0) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_GATHER, bufs, nranks, count, dtype, -1, root, stream);
+}
+
+ar_status_t ar_alltoall(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
+                        void* stream) {
+  if (nranks >= 1 && nranks <= AR_MAX_RANKS && count % static_cast<size_t>(nranks) != 0)
+    return AR_ERROR_INVALID_ARGUMENT;
+  return run(AR_ALLTOALL, bufs, nranks, count, dtype, -1, -1, stream);
 }
 
 ar_status_t ar_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, ar_op_t op,
@@ -269,6 +279,8 @@ ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar
   const bool rooted =
       coll == AR_BROADCAST || coll == AR_REDUCE || coll == AR_SCATTER || coll == AR_GATHER;
   if (rooted && (root < 0 || root >= nranks)) return AR_ERROR_INVALID_ARGUMENT;
+  if (coll == AR_ALLTOALL && count % static_cast<size_t>(nranks) != 0)
+    return AR_ERROR_INVALID_ARGUMENT;
   for (int r = 0; r < nranks; ++r) sent[r] = recv[r] = 0;
   const std::vector<ar::Step> sched = ar::schedule_for(coll, nranks, count, rooted ? root : 0);
   ar::count_bytes(sched, ar::itemsize(dtype), sent, recv);

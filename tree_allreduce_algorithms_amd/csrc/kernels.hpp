@@ -30,6 +30,11 @@ hipError_t launch_ring_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtyp
 hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
                          bool from_root, int root, bool vec, hipStream_t stream);
 
+// AllToAll: block j of rank i and block i of rank j swap places for every
+// pair i < j (count must be a multiple of n).
+hipError_t launch_alltoall(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype, bool vec,
+                           hipStream_t stream);
+
 // Fused binomial tree fold.  root < 0: the double tree, per element the
 // pairwise fold of the tree that owns it, stored into every rank.  root >= 0:
 // Reduce, one tree over the whole buffer on roles (rank - root) mod N, stored

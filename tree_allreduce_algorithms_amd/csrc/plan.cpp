@@ -141,6 +141,21 @@ std::vector<Step> scatter_schedule(int n, uint64_t count, int root, bool to_root
   return out;
 }
 
+// AllToAll: one step in which rank i sends its block j to rank j (block i
+// there), for every i != j.  Transfer ranges name the source block; the
+// kernel swaps block pairs instead of replaying these transfers.
+std::vector<Step> alltoall_schedule(int n, uint64_t count) {
+  std::vector<Step> out;
+  if (n < 2) return out;
+  const uint64_t b = count / static_cast<uint64_t>(n);
+  Step s{false, {}};
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j)
+      if (i != j) s.xfers.push_back({i, j, static_cast<uint64_t>(j) * b, static_cast<uint64_t>(j + 1) * b});
+  out.push_back(std::move(s));
+  return out;
+}
+
 std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int root) {
   switch (coll) {
     case AR_RING_ALLREDUCE: {
@@ -156,6 +171,7 @@ std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int 
     case AR_REDUCE: return reduce_schedule(n, count, root);
     case AR_SCATTER: return scatter_schedule(n, count, root, false);
     case AR_GATHER: return scatter_schedule(n, count, root, true);
+    case AR_ALLTOALL: return alltoall_schedule(n, count);
   }
   return {};
 }
@@ -179,14 +195,16 @@ int expected_steps(ar_collective_t coll, int n) {
     case AR_REDUCE: return tree_depth(n);
     case AR_TREE_ALLREDUCE: return 2 * tree_depth(n);
     case AR_SCATTER:
-    case AR_GATHER: return n > 1 ? 1 : 0;
+    case AR_GATHER:
+    case AR_ALLTOALL: return n > 1 ? 1 : 0;
   }
   return -1;
 }
 
 int impl_launches(ar_collective_t coll, ar_impl_t impl, int n) {
-  // Reduce has one (fused) implementation; Scatter and Gather are one step.
-  if (impl == AR_IMPL_FUSED || coll == AR_REDUCE) return n > 1 ? 1 : 0;
+  // Reduce has one (fused) implementation; Scatter, Gather and AllToAll are
+  // one step.
+  if (impl == AR_IMPL_FUSED || coll == AR_REDUCE || coll == AR_ALLTOALL) return n > 1 ? 1 : 0;
   return expected_steps(coll, n);
 }
 
@@ -195,9 +213,10 @@ uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t co
   const uint64_t un = static_cast<uint64_t>(n);
   // Scatter and Gather run their one schedule step under either
   // implementation (modelled with the root at rank 0); Reduce runs fused
-  // under either.
+  // under either; AllToAll reads and writes every off-diagonal block once
+  // (2 bytes moved per transferred byte, which its schedule gives).
   const bool fused = impl == AR_IMPL_FUSED || coll == AR_REDUCE;
-  if (fused && coll != AR_SCATTER && coll != AR_GATHER) {
+  if (fused && coll != AR_SCATTER && coll != AR_GATHER && coll != AR_ALLTOALL) {
     switch (coll) {
       case AR_RING_ALLREDUCE:
       case AR_TREE_ALLREDUCE: return 2 * un * count * isz;
@@ -219,6 +238,7 @@ ar_status_t validate(void* const* bufs, int n, size_t count, int dtype, int op, 
   if (root >= n) return AR_ERROR_INVALID_ARGUMENT;
   const size_t isz = itemsize(static_cast<ar_dtype_t>(dtype));
   if (count > SIZE_MAX / isz) return AR_ERROR_INVALID_ARGUMENT;
+  if (count == 0) return AR_SUCCESS;   // no element is touched: entries are not inspected
   const uint64_t bytes = static_cast<uint64_t>(count) * isz;
   std::pair<uintptr_t, int> order[AR_MAX_RANKS];
   for (int r = 0; r < n; ++r) {

@@ -50,6 +50,7 @@ std::vector<Step> tree_allreduce_schedule(int n, uint64_t count);
 std::vector<Step> broadcast_schedule(int n, uint64_t count, int root);
 std::vector<Step> reduce_schedule(int n, uint64_t count, int root);
 std::vector<Step> scatter_schedule(int n, uint64_t count, int root, bool to_root);
+std::vector<Step> alltoall_schedule(int n, uint64_t count);
 std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int root);
 
 // Adds the bytes of every transfer to sent[src] / recv[dst].
@@ -67,9 +68,10 @@ int impl_launches(ar_collective_t coll, ar_impl_t impl, int n);
 uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz);
 
 // Validation shared by every collective call.  `op` < 0 means "not used",
-// `root` < 0 means "not used".  Checks: bufs / entries non-NULL, n in range,
-// element alignment, count * itemsize overflow, pairwise overlap of the
-// [ptr, ptr + count * itemsize) ranges, dtype / op / root ranges.
+// `root` < 0 means "not used".  Checks: bufs non-NULL, n in range, dtype /
+// op / root ranges, count * itemsize overflow, and, when count > 0, entries
+// non-NULL, element alignment and pairwise overlap of the
+// [ptr, ptr + count * itemsize) ranges.
 ar_status_t validate(void* const* bufs, int n, size_t count, int dtype, int op, int root);
 
 }  // namespace ar

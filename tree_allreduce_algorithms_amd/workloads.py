@@ -13,6 +13,8 @@ stream):
 * ``large_grad_bf16``: the same draw rounded to bfloat16 (nearest-even).
 * ``sweep_<T>``: N=4 float32 uniform in [-1, 1), T in {256, 262144, 4194304, 67108864}.
 * ``zero_n64``: N=64, T=16,777,217 float32 Normal(0, 1) (N does not divide T).
+* ``moe_alltoall``: N=8, T=33,554,432 float32 Normal(0, 1): the AllToAll of an
+  expert-parallel token exchange, 8 blocks of 16 MiB per rank.
 
 Host draws use ``numpy.random.default_rng([seed, rank])``.  Device draws (for
 the sizes where a host draw plus upload would dominate a run) use a
@@ -57,6 +59,7 @@ WORKLOADS = {
     "large_grad_bf16": Workload("large_grad_bf16", 8, 300_000_000, "bfloat16", "normal", 3,
                                 {"std": 1e-3}),
     "zero_n64": Workload("zero_n64", 64, 16_777_217, "float32", "normal", 5, {"std": 1.0}),
+    "moe_alltoall": Workload("moe_alltoall", 8, 33_554_432, "float32", "normal", 6, {"std": 1.0}),
 }
 for _t in SWEEP_COUNTS:
     WORKLOADS[f"sweep_{_t}"] = Workload(f"sweep_{_t}", 4, _t, "float32", "uniform_pm1", 4)
