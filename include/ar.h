@@ -48,16 +48,19 @@
  *         (chunk c folds ranks c+1, c+2, ..., c); the tree call reproduces the
  *         binomial double tree's pairing.  Results are therefore bit-exact
  *         and independent of the implementation chosen by ar_set_impl().
- * Errors  reported synchronously BEFORE anything is enqueued, so a failing
- *         call has no effect:
+ * Errors  argument errors are reported synchronously BEFORE anything is
+ *         enqueued, so such a call has no effect:
  *           AR_ERROR_INVALID_ARGUMENT  bufs or an entry NULL; nranks out of
  *               range; a pointer not aligned to the element size; two buffer
  *               ranges overlapping; count * element size overflowing; root
  *               out of range; unknown dtype or op;
  *           AR_ERROR_UNSUPPORTED       a valid request this build lacks;
  *           AR_ERROR_HIP               a kernel launch failed; the hipError_t
- *               is kept for ar_last_hip_error().  (Faults during execution
- *               surface at the caller's next synchronisation.)
+ *               is kept for ar_last_hip_error().  With the step
+ *               implementation the launches of earlier steps may already be
+ *               enqueued, so the buffers are then unspecified.  (Faults
+ *               during execution surface at the caller's next
+ *               synchronisation.)
  *         count == 0 or nranks == 1 is a valid no-op (AR_SUCCESS, nothing
  *         enqueued); with count == 0 the entries of bufs are not inspected
  *         (an empty tensor may have a NULL data pointer).

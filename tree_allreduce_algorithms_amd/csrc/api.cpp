@@ -77,10 +77,10 @@ ar_collective_t choose_allreduce(int n, size_t count, ar_dtype_t dtype) {
   return tree < ring ? AR_TREE_ALLREDUCE : AR_RING_ALLREDUCE;
 }
 
-void add_counters(ar_collective_t coll, const std::vector<ar::Step>& sched, int n, size_t isz) {
-  uint64_t sent[AR_MAX_RANKS] = {};
-  uint64_t recv[AR_MAX_RANKS] = {};
-  ar::count_bytes(sched, isz, sent, recv);
+void add_counters(ar_collective_t coll, int n, uint64_t count, int root, size_t isz) {
+  uint64_t sent[AR_MAX_RANKS];
+  uint64_t recv[AR_MAX_RANKS];
+  ar::logical_bytes(coll, n, count, root < 0 ? 0 : root, isz, sent, recv);
   std::lock_guard<std::mutex> lock(g_counter_mu);
   for (int r = 0; r < n; ++r) {
     g_sent[r] += sent[r];
@@ -94,9 +94,8 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
   const ar_status_t v = ar::validate(bufs, n, count, static_cast<int>(dtype), op, root);
   if (v != AR_SUCCESS) return v;
   const ar_op_t aop = op >= 0 ? static_cast<ar_op_t>(op) : AR_SUM;
-  const std::vector<ar::Step> sched = ar::schedule_for(coll, n, count, root < 0 ? 0 : root);
   if (n == 1 || count == 0) {
-    add_counters(coll, sched, n, ar::itemsize(dtype));
+    add_counters(coll, n, count, root, ar::itemsize(dtype));
     return AR_SUCCESS;
   }
 
@@ -123,6 +122,8 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
   } else if (coll == AR_ALLTOALL) {
     err = ar::launch_alltoall(ptrs, n, count, dtype, vec, stream);
   } else if (impl == AR_IMPL_STEP || coll == AR_SCATTER || coll == AR_GATHER) {
+    // the literal schedule: one launch per step (the schedule is built only here)
+    const std::vector<ar::Step> sched = ar::schedule_for(coll, n, count, root < 0 ? 0 : root);
     for (const ar::Step& s : sched) {
       err = ar::launch_step(ptrs, s, dtype, aop, vec, stream);
       if (err != hipSuccess) break;
@@ -152,7 +153,7 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
     t_last_hip_error = static_cast<int>(err);
     return AR_ERROR_HIP;
   }
-  add_counters(coll, sched, n, ar::itemsize(dtype));
+  add_counters(coll, n, count, root, ar::itemsize(dtype));
   return AR_SUCCESS;
 }
 
@@ -281,9 +282,7 @@ ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar
   if (rooted && (root < 0 || root >= nranks)) return AR_ERROR_INVALID_ARGUMENT;
   if (coll == AR_ALLTOALL && count % static_cast<size_t>(nranks) != 0)
     return AR_ERROR_INVALID_ARGUMENT;
-  for (int r = 0; r < nranks; ++r) sent[r] = recv[r] = 0;
-  const std::vector<ar::Step> sched = ar::schedule_for(coll, nranks, count, rooted ? root : 0);
-  ar::count_bytes(sched, ar::itemsize(dtype), sent, recv);
+  ar::logical_bytes(coll, nranks, count, rooted ? root : 0, ar::itemsize(dtype), sent, recv);
   return AR_SUCCESS;
 }
 

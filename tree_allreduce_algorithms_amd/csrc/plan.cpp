@@ -176,6 +176,91 @@ std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int 
   return {};
 }
 
+namespace {
+
+// Binomial-tree traffic of role q in a tree over n roles: q sends its segment
+// to its parent once (q != 0) and receives one segment from each child.
+uint64_t tree_children(int q, int n) {
+  uint64_t c = 0;
+  for (int k = 0; (1 << k) < n; ++k) {
+    if (q % (1 << (k + 1)) != 0) break;
+    if (q + (1 << k) < n) ++c;
+  }
+  return c;
+}
+
+uint64_t chunk_len(int n, uint64_t count, int c) {
+  uint64_t lo, hi;
+  chunk_bounds(n, count, c, &lo, &hi);
+  return hi - lo;
+}
+
+}  // namespace
+
+void logical_bytes(ar_collective_t coll, int n, uint64_t count, int root, size_t isz,
+                   uint64_t* sent, uint64_t* recv) {
+  for (int r = 0; r < n; ++r) sent[r] = recv[r] = 0;
+  if (n < 2) return;
+  auto add = [&](uint64_t* v, int r, uint64_t elems) { v[r] += elems * isz; };
+  const bool rs = coll == AR_RING_ALLREDUCE || coll == AR_REDUCE_SCATTER;
+  const bool ag = coll == AR_RING_ALLREDUCE || coll == AR_ALLGATHER;
+  for (int r = 0; r < n; ++r) {
+    const int prev = (r + n - 1) % n, next = (r + 1) % n;
+    if (rs) {   // ReduceScatter: r sends every chunk but its own, gets every chunk but r-1's
+      add(sent, r, count - chunk_len(n, count, r));
+      add(recv, r, count - chunk_len(n, count, prev));
+    }
+    if (ag) {   // AllGather: r forwards every chunk but r+1's, gets every chunk but its own
+      add(sent, r, count - chunk_len(n, count, next));
+      add(recv, r, count - chunk_len(n, count, r));
+    }
+  }
+  switch (coll) {
+    case AR_TREE_ALLREDUCE: {   // both trees: reduce rounds then the mirrored broadcast rounds
+      const uint64_t h = tree_split(count);
+      for (int tree = 0; tree < 2; ++tree) {
+        const uint64_t seg = tree == 0 ? h : count - h;
+        for (int q = 0; q < n; ++q) {
+          const int r = tree_rank(tree, q, n);
+          const uint64_t moved = seg * (tree_children(q, n) + (q != 0 ? 1 : 0));
+          add(sent, r, moved);
+          add(recv, r, moved);
+        }
+      }
+      break;
+    }
+    case AR_BROADCAST:
+    case AR_REDUCE:   // one rooted tree over the whole buffer, one direction
+      for (int q = 0; q < n; ++q) {
+        const int r = (q + root) % n;
+        const uint64_t to_children = count * tree_children(q, n);
+        const uint64_t to_parent = q != 0 ? count : 0;
+        add(coll == AR_BROADCAST ? sent : recv, r, to_children);
+        add(coll == AR_BROADCAST ? recv : sent, r, to_parent);
+      }
+      break;
+    case AR_SCATTER:
+    case AR_GATHER:
+      for (int c = 0; c < n; ++c) {
+        if (c == root) continue;
+        const uint64_t len = chunk_len(n, count, c);
+        add(coll == AR_SCATTER ? sent : recv, root, len);
+        add(coll == AR_SCATTER ? recv : sent, c, len);
+      }
+      break;
+    case AR_ALLTOALL: {
+      const uint64_t b = count / static_cast<uint64_t>(n);
+      for (int r = 0; r < n; ++r) {
+        add(sent, r, b * static_cast<uint64_t>(n - 1));
+        add(recv, r, b * static_cast<uint64_t>(n - 1));
+      }
+      break;
+    }
+    default:
+      break;
+  }
+}
+
 void count_bytes(const std::vector<Step>& steps, size_t isz, uint64_t* sent, uint64_t* recv) {
   for (const Step& s : steps)
     for (const Transfer& x : s.xfers) {
@@ -211,10 +296,9 @@ int impl_launches(ar_collective_t coll, ar_impl_t impl, int n) {
 uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz) {
   if (n <= 1) return 0;
   const uint64_t un = static_cast<uint64_t>(n);
-  // Scatter and Gather run their one schedule step under either
-  // implementation (modelled with the root at rank 0); Reduce runs fused
-  // under either; AllToAll reads and writes every off-diagonal block once
-  // (2 bytes moved per transferred byte, which its schedule gives).
+  // Reduce runs fused under either implementation, AllToAll one swap kernel
+  // (every off-diagonal block read and written once); Scatter and Gather
+  // run their one schedule step under either (modelled with root 0).
   const bool fused = impl == AR_IMPL_FUSED || coll == AR_REDUCE;
   if (fused && coll != AR_SCATTER && coll != AR_GATHER && coll != AR_ALLTOALL) {
     switch (coll) {
@@ -225,10 +309,17 @@ uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t co
       default: return un * count * isz;   // AllGather, Broadcast
     }
   }
-  uint64_t bytes = 0;
-  for (const Step& s : schedule_for(coll, n, count, 0))
-    for (const Transfer& x : s.xfers) bytes += (x.hi - x.lo) * isz * (s.reduce ? 3 : 2);
-  return bytes;
+  // The literal schedule: 3 bytes per element of each reduce transfer (read
+  // both sides, write one), 2 per element of each copy transfer.
+  uint64_t sent[AR_MAX_RANKS];
+  uint64_t recv[AR_MAX_RANKS];
+  logical_bytes(coll, n, count, 0, 1, sent, recv);
+  uint64_t moved = 0;
+  for (int r = 0; r < n; ++r) moved += sent[r];
+  uint64_t reduced = 0;
+  if (coll == AR_RING_ALLREDUCE || coll == AR_TREE_ALLREDUCE) reduced = moved / 2;
+  if (coll == AR_REDUCE_SCATTER) reduced = moved;
+  return (3 * reduced + 2 * (moved - reduced)) * isz;
 }
 
 ar_status_t validate(void* const* bufs, int n, size_t count, int dtype, int op, int root) {

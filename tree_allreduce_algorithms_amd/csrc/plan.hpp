@@ -56,6 +56,11 @@ std::vector<Step> schedule_for(ar_collective_t coll, int n, uint64_t count, int 
 // Adds the bytes of every transfer to sent[src] / recv[dst].
 void count_bytes(const std::vector<Step>& steps, size_t isz, uint64_t* sent, uint64_t* recv);
 
+// The same per-rank totals as count_bytes over schedule_for(coll, ...), from
+// closed forms, without building the schedule (sent / recv are overwritten).
+void logical_bytes(ar_collective_t coll, int n, uint64_t count, int root, size_t isz,
+                   uint64_t* sent, uint64_t* recv);
+
 int expected_steps(ar_collective_t coll, int n);
 
 // Kernel launches and HBM bytes of one call of `coll` with implementation
