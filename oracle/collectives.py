@@ -32,7 +32,9 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .numerics import ITEMSIZE, STORAGE, combine
+from .numerics import ITEMSIZE, STORAGE, bf16_to_f32, combine, f32_to_bf16_rne
+
+ACC32 = "bfloat16_acc32"
 
 
 @dataclass
@@ -135,6 +137,19 @@ def _count(sent, recv, src, dst, nelem, dtype):
     recv[dst] += nbytes
 
 
+def _float32_partials(x, run):
+    """bfloat16 buffers whose reductions carry float32 partials: every rank is
+    widened to float32 (exact), the float32 schedule runs unchanged (same
+    steps, same order, each hop one float32 operation), and every buffer is
+    rounded back to bfloat16 once, to nearest even.  A buffer the schedule
+    does not write comes back with its bits (a widened bfloat16 rounds to
+    itself; a signalling NaN would come back quiet).  Counters count the
+    stored 2-byte elements."""
+    res = run([bf16_to_f32(a) for a in x])
+    bufs = [f32_to_bf16_rne(b) for b in res.bufs]
+    return Result(bufs, res.sent // np.uint64(2), res.recv // np.uint64(2), res.steps)
+
+
 # --- ring --------------------------------------------------------------------
 
 def _ring_reduce_scatter_steps(bufs, sent, recv, span, op, dtype):
@@ -173,6 +188,9 @@ def ring_reduce_scatter(x, op, dtype, window_start=0, total=None):
     """Ring ReduceScatter: N-1 steps; afterwards rank r's chunk r holds the
     reduction of chunk r over all ranks, folded in ring order (starting at rank
     r+1, ending at rank r).  Other chunks hold partial results."""
+    if dtype == ACC32:
+        return _float32_partials(
+            x, lambda w: ring_reduce_scatter(w, op, "float32", window_start, total))
     n, length, total, bufs, sent, recv = _setup(x, dtype, window_start, total)
     steps = _ring_reduce_scatter_steps(
         bufs, sent, recv, _ring_spans(n, total, window_start, length), op, dtype)
@@ -192,6 +210,9 @@ def ring_allreduce(x, op, dtype, window_start=0, total=None):
     """Ring AllReduce = ReduceScatter then AllGather on the same buffers
     (Lecture 09 sections 3.9 and 4.3; Collectives from scratch, two-pass ring):
     2(N-1) steps, every rank ends with the same reduction."""
+    if dtype == ACC32:
+        return _float32_partials(
+            x, lambda w: ring_allreduce(w, op, "float32", window_start, total))
     n, length, total, bufs, sent, recv = _setup(x, dtype, window_start, total)
     span = _ring_spans(n, total, window_start, length)
     steps = _ring_reduce_scatter_steps(bufs, sent, recv, span, op, dtype)
@@ -225,6 +246,9 @@ def tree_allreduce(x, op, dtype, trees=2, window_start=0, total=None):
     role == rank, tree 1 handles the rest with role == N-1-rank; both run their
     rounds in the same steps.  ``trees=1``: one tree over all T elements.
     """
+    if dtype == ACC32:
+        return _float32_partials(
+            x, lambda w: tree_allreduce(w, op, "float32", trees, window_start, total))
     n, length, total, bufs, sent, recv = _setup(x, dtype, window_start, total)
     segs = [(tree, _local(lo, hi, window_start, length))
             for tree, lo, hi in _tree_segments(trees, total)]
@@ -294,6 +318,9 @@ def reduce(x, root, op, dtype, window_start=0, total=None):
     the root's buffer takes the root's working copy; the other buffers are
     unchanged, as section 3.4 requires.
     """
+    if dtype == ACC32:
+        return _float32_partials(
+            x, lambda w: reduce(w, root, op, "float32", window_start, total))
     n, length, total, bufs, sent, recv = _setup(x, dtype, window_start, total)
     if not 0 <= root < n:
         raise ValueError("root out of range")

@@ -19,14 +19,20 @@ readings here are:
 * MAX keeps the local value unless the incoming one compares strictly greater;
   MIN unless strictly smaller.  That fixes which zero survives a +0/-0 tie and
   that a NaN on the incoming side never wins.
+* bfloat16_acc32: bfloat16 buffers whose reductions carry float32 partials
+  from hop to hop and round once at the end (the "bf16 with fp32
+  accumulation" variant).  It is not a per-hop rule, so ``combine`` refuses
+  it; the collectives widen to float32, run the float32 schedule and round
+  (``collectives._float32_partials``).
 """
 
 import numpy as np
 
-DTYPES = ("int32", "float32", "bfloat16")
+DTYPES = ("int32", "float32", "bfloat16", "bfloat16_acc32")
 OPS = ("sum", "prod", "max", "min")
-ITEMSIZE = {"int32": 4, "float32": 4, "bfloat16": 2}
-STORAGE = {"int32": np.int32, "float32": np.float32, "bfloat16": np.uint16}
+ITEMSIZE = {"int32": 4, "float32": 4, "bfloat16": 2, "bfloat16_acc32": 2}
+STORAGE = {"int32": np.int32, "float32": np.float32, "bfloat16": np.uint16,
+           "bfloat16_acc32": np.uint16}
 
 
 def bf16_to_f32(bits):
@@ -93,4 +99,6 @@ def combine(local, incoming, op, dtype):
         if op == "max":
             return np.where(b > a, bbits, abits).astype(np.uint16)
         return np.where(b < a, bbits, abits).astype(np.uint16)
+    if dtype == "bfloat16_acc32":
+        raise ValueError("bfloat16_acc32 has no per-hop rule: its partials are float32")
     raise ValueError(f"unknown dtype {dtype!r}")
