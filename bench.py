@@ -3,7 +3,7 @@ MI355X, through the C ABI of libar.so.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3]
                     [--workload large_grad_fp32] [--collective ring_allreduce]
-                    [--impl fused|step] [--flush-mall]
+                    [--impl fused|step] [--flush-mall] [--accumulate float32]
                     [--no-cpu-baseline] [--no-parity] [--suite FILE.jsonl]
 
 One "step" is one collective call over the whole workload (every rank buffer
@@ -78,7 +78,9 @@ def parse(argv=None):
     p.add_argument("--workload", default="large_grad_fp32")
     p.add_argument("--collective", default="ring_allreduce", choices=COLLECTIVES)
     p.add_argument("--impl", default="fused", choices=["fused", "step"])
-    p.add_argument("--root", type=int, default=0, help="broadcast root")
+    p.add_argument("--root", type=int, default=0, help="root of the rooted collectives")
+    p.add_argument("--accumulate", default=None, choices=[None, "float32"],
+                   help="bfloat16 workloads: reductions carry float32 partials, round once")
     p.add_argument("--flush-mall", action="store_true")
     p.add_argument("--cpu-window", type=int, default=1 << 24,
                    help="elements per rank per window of the CPU checker")
@@ -150,7 +152,7 @@ def step_bytes(collective, n, t, isz):
     return (3 * reduced + 2 * (moved - reduced)) * isz
 
 
-def run_checker(collective, pristine, got, w, root, window):
+def run_checker(collective, pristine, got, w, root, window, odt=None):
     """Run the CPU checker over every window of the workload on the inputs in
     `pristine`, compare with the device output `got`; returns (seconds,
     compared elements, mismatching elements)."""
@@ -159,6 +161,7 @@ def run_checker(collective, pristine, got, w, root, window):
     import torch
 
     n, t = w.nranks, w.count
+    odt = odt or w.dtype          # the oracle's dtype name
     owned = oracle.chunk_layout(n, t)
 
     def host(x, a, b):
@@ -168,15 +171,15 @@ def run_checker(collective, pristine, got, w, root, window):
         return v.cpu().numpy()
 
     fn = {
-        "ring_allreduce": lambda x, a: oracle.ring_allreduce(x, "sum", w.dtype, a, t),
-        "tree_allreduce": lambda x, a: oracle.tree_allreduce(x, "sum", w.dtype, 2, a, t),
-        "reduce_scatter": lambda x, a: oracle.ring_reduce_scatter(x, "sum", w.dtype, a, t),
-        "allgather": lambda x, a: oracle.ring_allgather(x, w.dtype, a, t),
-        "broadcast": lambda x, a: oracle.broadcast(x, root, w.dtype, a, t),
-        "reduce": lambda x, a: oracle.reduce(x, root, "sum", w.dtype, a, t),
-        "scatter": lambda x, a: oracle.scatter(x, root, w.dtype, a, t),
-        "gather": lambda x, a: oracle.gather(x, root, w.dtype, a, t),
-        "alltoall": lambda x, a: oracle.alltoall(x, w.dtype),
+        "ring_allreduce": lambda x, a: oracle.ring_allreduce(x, "sum", odt, a, t),
+        "tree_allreduce": lambda x, a: oracle.tree_allreduce(x, "sum", odt, 2, a, t),
+        "reduce_scatter": lambda x, a: oracle.ring_reduce_scatter(x, "sum", odt, a, t),
+        "allgather": lambda x, a: oracle.ring_allgather(x, odt, a, t),
+        "broadcast": lambda x, a: oracle.broadcast(x, root, odt, a, t),
+        "reduce": lambda x, a: oracle.reduce(x, root, "sum", odt, a, t),
+        "scatter": lambda x, a: oracle.scatter(x, root, odt, a, t),
+        "gather": lambda x, a: oracle.gather(x, root, odt, a, t),
+        "alltoall": lambda x, a: oracle.alltoall(x, odt),
     }[collective]
     if collective == "alltoall":
         window = t   # an output element comes from another position: whole buffers
@@ -220,17 +223,21 @@ def run_one(args):
 
     bufs = draw()
     torch.cuda.synchronize()
+    if args.accumulate and w.dtype != "bfloat16":
+        raise SystemExit("--accumulate float32 applies to bfloat16 workloads")
+    acc = args.accumulate
+    odt = "bfloat16_acc32" if acc else w.dtype     # library / oracle dtype name
     # "allreduce" runs the ring or the tree by the library's cost model
-    ran = (ar.allreduce_choice(n, t, w.dtype) if args.collective == "allreduce"
+    ran = (ar.allreduce_choice(n, t, odt) if args.collective == "allreduce"
            else args.collective)
     call = {
-        "allreduce": lambda b: ar.allreduce(b),
-        "ring_allreduce": lambda b: ar.ring_allreduce(b),
-        "tree_allreduce": lambda b: ar.tree_allreduce(b),
-        "reduce_scatter": lambda b: ar.reduce_scatter(b),
+        "allreduce": lambda b: ar.allreduce(b, accumulate=acc),
+        "ring_allreduce": lambda b: ar.ring_allreduce(b, accumulate=acc),
+        "tree_allreduce": lambda b: ar.tree_allreduce(b, accumulate=acc),
+        "reduce_scatter": lambda b: ar.reduce_scatter(b, accumulate=acc),
         "allgather": lambda b: ar.allgather(b),
         "broadcast": lambda b: ar.broadcast(b, root=args.root),
-        "reduce": lambda b: ar.reduce(b, root=args.root),
+        "reduce": lambda b: ar.reduce(b, root=args.root, accumulate=acc),
         "scatter": lambda b: ar.scatter(b, root=args.root),
         "gather": lambda b: ar.gather(b, root=args.root),
         "alltoall": lambda b: ar.alltoall(b),
@@ -266,9 +273,12 @@ def run_one(args):
     launch_ms = sum(event_ms) / len(event_ms)
     per_call_s = (launch_ms * 1e-3) if args.flush_mall else wall / args.steps
     alg = algorithmic_bytes(ran, n, t, isz)
-    launches = (1 if args.impl == "fused" or ran in ("reduce", "alltoall")
-                else ar.expected_steps(ran, n))
-    moved = alg if args.impl == "fused" else step_bytes(ran, n, t, isz)
+    # Reduce and AllToAll have one implementation; with float32 partials the
+    # reductions run fused under either implementation
+    fused = (args.impl == "fused" or ran in ("reduce", "alltoall")
+             or (acc is not None and ran in ("ring_allreduce", "reduce_scatter", "tree_allreduce")))
+    launches = 1 if fused else ar.expected_steps(ran, n)
+    moved = alg if fused else step_bytes(ran, n, t, isz)
     achieved = moved / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(w.name, args.collective, args.impl)
 
@@ -286,7 +296,7 @@ def run_one(args):
         "dtype": DTYPE_TAG[w.dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "collective": args.collective, "ran": ran,
-                   "impl": args.impl,
+                   "impl": args.impl, "accumulate": acc or w.dtype,
                    "nranks": n, "count_per_rank": t, "rank_bytes": t * isz,
                    "distribution": w.dist, "params": w.params, "seed": w.seed,
                    "timing": "events, Infinity Cache flushed before each call"
@@ -338,7 +348,7 @@ def run_one(args):
         got = [p.clone() for p in pristine]
         call(got)
         torch.cuda.synchronize()
-        secs, compared, bad = run_checker(ran, pristine, got, w, args.root, args.cpu_window)
+        secs, compared, bad = run_checker(ran, pristine, got, w, args.root, args.cpu_window, odt)
         del pristine, got
         torch.cuda.empty_cache()
         windows = -(-t // args.cpu_window)
@@ -365,6 +375,7 @@ SUITE = [
     ("large_grad_fp32", "tree_allreduce", "fused", []),
     ("large_grad_bf16", "ring_allreduce", "fused", []),
     ("large_grad_bf16", "ring_allreduce", "step", []),
+    ("large_grad_bf16", "ring_allreduce", "fused", ["--accumulate", "float32"]),
     ("ddp_bucket", "ring_allreduce", "fused", []),
     ("ddp_bucket", "ring_allreduce", "fused", ["--flush-mall"]),
     ("ddp_bucket", "ring_allreduce", "step", ["--flush-mall"]),

@@ -89,7 +89,19 @@ typedef enum {
   AR_ERROR_HIP = 3
 } ar_status_t;
 
-typedef enum { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BFLOAT16 = 2 } ar_dtype_t;
+/* AR_BFLOAT16_ACC32: bfloat16 buffers ("bf16 with fp32 accumulation").  The
+ * reductions (ring AllReduce and ReduceScatter, tree AllReduce, Reduce)
+ * carry float32 partials from hop to hop in the schedule's own order and
+ * round to bfloat16 once, at the end; a partial cannot live in a bfloat16
+ * buffer between kernel launches, so these reductions run fused under either
+ * implementation.  Copies (AllGather, Broadcast, Scatter, Gather, AllToAll)
+ * are bfloat16 copies.  Elements count 2 bytes in every byte counter. */
+typedef enum {
+  AR_INT32 = 0,
+  AR_FLOAT32 = 1,
+  AR_BFLOAT16 = 2,
+  AR_BFLOAT16_ACC32 = 3
+} ar_dtype_t;
 
 /* The reduction operators listed in [L09 3.4]. */
 typedef enum { AR_SUM = 0, AR_PROD = 1, AR_MAX = 2, AR_MIN = 3 } ar_op_t;

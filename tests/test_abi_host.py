@@ -75,7 +75,7 @@ ORACLE_CALLS = {
 @pytest.mark.parametrize("coll", sorted(ORACLE_CALLS))
 @pytest.mark.parametrize("n,t", [(1, 10), (2, 9), (3, 7), (4, 1024), (5, 23), (8, 1000),
                                  (8, 3), (16, 37), (64, 130), (64, 1000), (6, 0)])
-@pytest.mark.parametrize("dtype", ["int32", "bfloat16"])
+@pytest.mark.parametrize("dtype", ["int32", "bfloat16", "bfloat16_acc32"])
 def test_expected_bytes_and_steps_match_oracle(coll, n, t, dtype):
     root = (n - 1) // 2
     if coll == "alltoall" and t % n:
@@ -84,7 +84,7 @@ def test_expected_bytes_and_steps_match_oracle(coll, n, t, dtype):
         return
     x = [np.zeros(t, np.int32) for _ in range(n)]
     res = ORACLE_CALLS[coll](x, root)
-    scale = 2 if dtype == "bfloat16" else 4
+    scale = oracle.ITEMSIZE[dtype]
     sent, recv = ar.expected_bytes(coll, n, t, dtype, root=root)
     assert sent == [int(v) // 4 * scale for v in res.sent]
     assert recv == [int(v) // 4 * scale for v in res.recv]

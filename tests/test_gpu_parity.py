@@ -592,3 +592,79 @@ def test_alltoall_block_sizes_and_involution():
         torch.cuda.synchronize()
         for r in range(n):
             assert_same(to_host(bufs[r], dtype), x[r], dtype, f"involution n={n} b={b} rank {r}")
+
+
+
+# --- bfloat16 buffers with float32 partials ---------------------------------------
+
+ACC32_CALLS = {
+    "ring_allreduce": (lambda b, op, root: ar.ring_allreduce(b, op=op, accumulate="float32"),
+                       lambda x, op, root: oracle.ring_allreduce(x, op, "bfloat16_acc32")),
+    "reduce_scatter": (lambda b, op, root: ar.reduce_scatter(b, op=op, accumulate="float32"),
+                       lambda x, op, root: oracle.ring_reduce_scatter(x, op, "bfloat16_acc32")),
+    "tree_allreduce": (lambda b, op, root: ar.tree_allreduce(b, op=op, accumulate="float32"),
+                       lambda x, op, root: oracle.tree_allreduce(x, op, "bfloat16_acc32")),
+    "reduce": (lambda b, op, root: ar.reduce(b, op=op, root=root, accumulate="float32"),
+               lambda x, op, root: oracle.reduce(x, root, op, "bfloat16_acc32")),
+}
+
+
+@pytest.mark.parametrize("coll", sorted(ACC32_CALLS))
+@pytest.mark.parametrize("shape", [(8, 100_003), (64, 20_011), (5, 23), (8, 3), (2, 4_099)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_acc32_parity(coll, shape):
+    """accumulate='float32' on bfloat16 buffers against the oracle's float32
+    schedule rounded once, bit for bit, for every op; the same result under
+    the step implementation (these reductions run fused for this dtype)."""
+    n, t = shape
+    x = workloads.host_inputs(n, t, "bfloat16", "uniform_pm1", 81 + n, {})
+    owned = oracle.chunk_layout(n, t)
+    root = n // 2
+    for op in ("sum", "prod", "max", "min"):
+        want = ACC32_CALLS[coll][1](x, op, root).bufs
+        for impl in IMPLS:
+            announce(f"acc32 {coll} n={n} t={t} op={op} impl={impl}")
+            ar.set_impl(impl)
+            bufs = to_dev(x, "bfloat16")
+            ACC32_CALLS[coll][0](bufs, op, root)
+            torch.cuda.synchronize()
+            for r in range(n):
+                got = to_host(bufs[r], "bfloat16")
+                if coll == "reduce_scatter":
+                    lo, hi = owned[r]
+                    assert_same(got[lo:hi], want[r][lo:hi], "bfloat16", f"{coll}/{op}/{impl} rank {r}")
+                else:
+                    assert_same(got, want[r], "bfloat16", f"{coll}/{op}/{impl} rank {r}")
+    ar.set_impl("fused")
+
+
+def test_acc32_large_gradient_windows():
+    """N=8 x 300,000,000 bfloat16, float32 partials: sampled windows against the
+    oracle; every rank identical."""
+    w = workloads.WORKLOADS["large_grad_bf16"]
+    bufs = _device_inputs(w)
+    size = -(-w.count // w.nranks)
+    wins = _windows(w.count, [c * size for c in range(1, w.nranks)], 3)
+    saved = [(a, b, _window_host(bufs, a, b, "bfloat16")) for a, b in wins]
+    ar.ring_allreduce(bufs, accumulate="float32")
+    torch.cuda.synchronize()
+    for a, b, xin in saved:
+        want = oracle.ring_allreduce(xin, "sum", "bfloat16_acc32", window_start=a, total=w.count).bufs
+        for r in (0, 4, 7):
+            assert_same(to_host(bufs[r][a:b], "bfloat16"), want[r], "bfloat16", f"window {a} rank {r}")
+    assert _ranks_identical(bufs)
+    del bufs
+    torch.cuda.empty_cache()
+
+
+def test_accumulate_option_is_validated():
+    ints = [torch.zeros(16, dtype=torch.int32, device=DEV) for _ in range(2)]
+    with pytest.raises(ValueError):
+        ar.ring_allreduce(ints, accumulate="float32")      # only bfloat16 buffers offer it
+    bf = [torch.zeros(16, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    with pytest.raises(ValueError):
+        ar.ring_allreduce(bf, accumulate="int32")
+    floats = [torch.ones(16, device=DEV) for _ in range(2)]
+    ar.ring_allreduce(floats, accumulate="float32")       # the buffers' own dtype: the default
+    torch.cuda.synchronize()
+    assert torch.equal(floats[0], torch.full((16,), 2.0, device=DEV))

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libar.so")
 MAX_RANKS = 64
 
 SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, HIP_ERROR = 0, 1, 2, 3
-DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
+DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2, "bfloat16_acc32": 3}
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 COLLECTIVES = {"ring_allreduce": 0, "reduce_scatter": 1, "allgather": 2, "broadcast": 3,
                "tree_allreduce": 4, "reduce": 5, "scatter": 6, "gather": 7, "alltoall": 8}
@@ -153,22 +153,31 @@ def _stream_handle(tensors, stream):
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _collective(name, tensors, op=None, root=None, stream=None):
+def _collective(name, tensors, op=None, root=None, stream=None, accumulate=None):
     tensors, dtype, count = _prep(tensors)
+    if accumulate not in (None, dtype):
+        if accumulate != "float32" or dtype != "bfloat16":
+            raise ValueError(f"accumulate={accumulate!r} is only offered as 'float32' for "
+                             f"bfloat16 buffers (got {dtype})")
+        dtype = "bfloat16_acc32"
     status = raw_call(name, [t.data_ptr() for t in tensors], count, dtype, op=op, root=root,
                       stream=_stream_handle(tensors, stream))
     _check(status, name)
     return tensors
 
 
-def ring_allreduce(tensors, op="sum", stream=None):
+# accumulate="float32" (bfloat16 buffers only): the reduction carries float32
+# partials from hop to hop in the schedule's order and rounds to bfloat16 once
+# (AR_BFLOAT16_ACC32); by default every hop rounds to the buffers' dtype.
+
+def ring_allreduce(tensors, op="sum", stream=None, accumulate=None):
     """Ring AllReduce in place over the rank tensors (see ar_ring_allreduce)."""
-    return _collective("ring_allreduce", tensors, op=op, stream=stream)
+    return _collective("ring_allreduce", tensors, op=op, stream=stream, accumulate=accumulate)
 
 
-def reduce_scatter(tensors, op="sum", stream=None):
+def reduce_scatter(tensors, op="sum", stream=None, accumulate=None):
     """Ring ReduceScatter in place: chunk r of tensors[r] ends fully reduced."""
-    return _collective("reduce_scatter", tensors, op=op, stream=stream)
+    return _collective("reduce_scatter", tensors, op=op, stream=stream, accumulate=accumulate)
 
 
 def allgather(tensors, stream=None):
@@ -181,14 +190,14 @@ def broadcast(tensors, root=0, stream=None):
     return _collective("broadcast", tensors, root=root, stream=stream)
 
 
-def tree_allreduce(tensors, op="sum", stream=None):
+def tree_allreduce(tensors, op="sum", stream=None, accumulate=None):
     """Double-binary-tree AllReduce in place (see ar_tree_allreduce)."""
-    return _collective("tree_allreduce", tensors, op=op, stream=stream)
+    return _collective("tree_allreduce", tensors, op=op, stream=stream, accumulate=accumulate)
 
 
-def reduce(tensors, op="sum", root=0, stream=None):
+def reduce(tensors, op="sum", root=0, stream=None, accumulate=None):
     """Reduce in place into tensors[root]; the other tensors keep their data."""
-    return _collective("reduce", tensors, op=op, root=root, stream=stream)
+    return _collective("reduce", tensors, op=op, root=root, stream=stream, accumulate=accumulate)
 
 
 def scatter(tensors, root=0, stream=None):
@@ -206,10 +215,10 @@ def alltoall(tensors, stream=None):
     return _collective("alltoall", tensors, stream=stream)
 
 
-def allreduce(tensors, op="sum", stream=None):
+def allreduce(tensors, op="sum", stream=None, accumulate=None):
     """AllReduce in place by the ring or the double tree, whichever the cost
     model predicts faster for this size (see ar_allreduce)."""
-    return _collective("allreduce", tensors, op=op, stream=stream)
+    return _collective("allreduce", tensors, op=op, stream=stream, accumulate=accumulate)
 
 
 # --- host-only helpers --------------------------------------------------------

@@ -60,6 +60,9 @@ bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_ALLTOALL
 bool impl_ok(int impl) { return impl == AR_IMPL_FUSED || impl == AR_IMPL_STEP; }
 
 double predict_us(ar_collective_t coll, ar_impl_t impl, int n, size_t count, ar_dtype_t dtype) {
+  if (dtype == AR_BFLOAT16_ACC32 &&
+      (coll == AR_RING_ALLREDUCE || coll == AR_REDUCE_SCATTER || coll == AR_TREE_ALLREDUCE))
+    impl = AR_IMPL_FUSED;   // these reductions run fused for this dtype
   CostCoeff c;
   {
     std::lock_guard<std::mutex> lock(g_cost_mu);
@@ -91,6 +94,8 @@ void add_counters(ar_collective_t coll, int n, uint64_t count, int root, size_t 
 
 ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar_dtype_t dtype,
                 int op, int root, void* stream_ptr) {
+  // dtype may be rewritten below (bfloat16 copies); counters use its size,
+  // which the rewrite keeps
   const ar_status_t v = ar::validate(bufs, n, count, static_cast<int>(dtype), op, root);
   if (v != AR_SUCCESS) return v;
   const ar_op_t aop = op >= 0 ? static_cast<ar_op_t>(op) : AR_SUM;
@@ -107,7 +112,15 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
     aligned16 = aligned16 && (reinterpret_cast<uintptr_t>(bufs[r]) % 16 == 0);
   }
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const ar_impl_t impl = static_cast<ar_impl_t>(g_impl.load());
+  // bfloat16 with float32 partials: the reductions can only run fused (a
+  // partial cannot live in a bfloat16 buffer between launches); the copies
+  // are bfloat16 copies.
+  const bool acc32 = dtype == AR_BFLOAT16_ACC32;
+  const bool reduction = coll == AR_RING_ALLREDUCE || coll == AR_REDUCE_SCATTER ||
+                         coll == AR_TREE_ALLREDUCE || coll == AR_REDUCE;
+  const ar_impl_t impl =
+      (acc32 && reduction) ? AR_IMPL_FUSED : static_cast<ar_impl_t>(g_impl.load());
+  if (acc32 && !reduction) dtype = AR_BFLOAT16;
 
   // 16-byte packs need every buffer 16-byte aligned (pack p of every rank
   // then covers the same elements); otherwise the kernels move one element

@@ -45,6 +45,7 @@ template <ar_dtype_t DT> struct Elem;
 template <> struct Elem<AR_INT32> { using T = int32_t; };
 template <> struct Elem<AR_FLOAT32> { using T = float; };
 template <> struct Elem<AR_BFLOAT16> { using T = uint16_t; };
+template <> struct Elem<AR_BFLOAT16_ACC32> { using T = uint16_t; };
 
 __device__ __forceinline__ float bf16_widen(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -145,6 +146,47 @@ __device__ __forceinline__ Pack<T, K> combine(const Pack<T, K>& local, const Pac
     return r;
   }
 }
+
+// How a fold accumulates.  Every dtype but AR_BFLOAT16_ACC32 folds in its
+// own element type (each hop is `combine`, rounding to that type); for
+// AR_BFLOAT16_ACC32 the loaded bfloat16 values are widened to float32, the
+// hops are float32 operations, and the result is rounded to bfloat16 once.
+// combine(local, incoming) keeps the receiver-side operand order.
+template <ar_dtype_t DT, ar_op_t OP, class P> struct Fold {
+  using A = P;
+  static __device__ __forceinline__ A widen(const P& p) { return p; }
+  static __device__ __forceinline__ P narrow(const A& a) { return a; }
+  static __device__ __forceinline__ A combine(const A& local, const A& incoming) {
+    return ::ar::combine<DT, OP>(local, incoming);
+  }
+};
+
+template <ar_op_t OP, int K> struct Fold<AR_BFLOAT16_ACC32, OP, Pack<uint16_t, K>> {
+  using P = Pack<uint16_t, K>;
+  using A = Pack<float, K>;
+  static __device__ __forceinline__ A widen(const P& p) {
+    A a;
+#pragma unroll
+    for (int j = 0; j < K; ++j) a.e[j] = bf16_widen(p.e[j]);
+    return a;
+  }
+  static __device__ __forceinline__ P narrow(const A& a) {
+    if constexpr (K % 2 == 0) {
+      Words<K / 2> w;
+#pragma unroll
+      for (int j = 0; j < K / 2; ++j) w.w[j] = bf16x2_round(a.e[2 * j], a.e[2 * j + 1]);
+      return __builtin_bit_cast(P, w);
+    } else {
+      P p;
+#pragma unroll
+      for (int j = 0; j < K; ++j) p.e[j] = bf16_round(a.e[j]);
+      return p;
+    }
+  }
+  static __device__ __forceinline__ A combine(const A& local, const A& incoming) {
+    return ::ar::combine<AR_FLOAT32, OP>(local, incoming);
+  }
+};
 
 // Plain element accesses (the unaligned head and tail of a segment).
 template <class P> __device__ __forceinline__ P load(const void* base, uint64_t i) {
@@ -306,33 +348,35 @@ hipError_t launch(const void* fn, dim3 grid, const Args& args, hipStream_t strea
 }
 
 // dtype x op dispatch onto a template taking <ar_dtype_t, ar_op_t>.
+// AR_DISPATCH covers the per-hop dtypes (the step kernels);
+// AR_DISPATCH_FOLD also covers AR_BFLOAT16_ACC32 (the fused folds).
+#define AR_DISPATCH_OPS(FN, DT, OP, ...)                                         \
+  switch (OP) {                                                                   \
+    case AR_SUM: return FN<DT, AR_SUM>(__VA_ARGS__);                              \
+    case AR_PROD: return FN<DT, AR_PROD>(__VA_ARGS__);                            \
+    case AR_MAX: return FN<DT, AR_MAX>(__VA_ARGS__);                              \
+    case AR_MIN: return FN<DT, AR_MIN>(__VA_ARGS__);                              \
+  }
+
 #define AR_DISPATCH(FN, DTYPE, OP, ...)                                          \
   do {                                                                            \
     switch (DTYPE) {                                                              \
-      case AR_INT32:                                                              \
-        switch (OP) {                                                             \
-          case AR_SUM: return FN<AR_INT32, AR_SUM>(__VA_ARGS__);                  \
-          case AR_PROD: return FN<AR_INT32, AR_PROD>(__VA_ARGS__);                \
-          case AR_MAX: return FN<AR_INT32, AR_MAX>(__VA_ARGS__);                  \
-          case AR_MIN: return FN<AR_INT32, AR_MIN>(__VA_ARGS__);                  \
-        }                                                                         \
-        break;                                                                    \
-      case AR_FLOAT32:                                                            \
-        switch (OP) {                                                             \
-          case AR_SUM: return FN<AR_FLOAT32, AR_SUM>(__VA_ARGS__);                \
-          case AR_PROD: return FN<AR_FLOAT32, AR_PROD>(__VA_ARGS__);              \
-          case AR_MAX: return FN<AR_FLOAT32, AR_MAX>(__VA_ARGS__);                \
-          case AR_MIN: return FN<AR_FLOAT32, AR_MIN>(__VA_ARGS__);                \
-        }                                                                         \
-        break;                                                                    \
-      case AR_BFLOAT16:                                                           \
-        switch (OP) {                                                             \
-          case AR_SUM: return FN<AR_BFLOAT16, AR_SUM>(__VA_ARGS__);               \
-          case AR_PROD: return FN<AR_BFLOAT16, AR_PROD>(__VA_ARGS__);             \
-          case AR_MAX: return FN<AR_BFLOAT16, AR_MAX>(__VA_ARGS__);               \
-          case AR_MIN: return FN<AR_BFLOAT16, AR_MIN>(__VA_ARGS__);               \
-        }                                                                         \
-        break;                                                                    \
+      case AR_INT32: AR_DISPATCH_OPS(FN, AR_INT32, OP, __VA_ARGS__) break;        \
+      case AR_FLOAT32: AR_DISPATCH_OPS(FN, AR_FLOAT32, OP, __VA_ARGS__) break;    \
+      case AR_BFLOAT16: AR_DISPATCH_OPS(FN, AR_BFLOAT16, OP, __VA_ARGS__) break;  \
+      default: break;                                                             \
+    }                                                                             \
+    return hipErrorInvalidValue;                                                  \
+  } while (0)
+
+#define AR_DISPATCH_FOLD(FN, DTYPE, OP, ...)                                     \
+  do {                                                                            \
+    switch (DTYPE) {                                                              \
+      case AR_INT32: AR_DISPATCH_OPS(FN, AR_INT32, OP, __VA_ARGS__) break;        \
+      case AR_FLOAT32: AR_DISPATCH_OPS(FN, AR_FLOAT32, OP, __VA_ARGS__) break;    \
+      case AR_BFLOAT16: AR_DISPATCH_OPS(FN, AR_BFLOAT16, OP, __VA_ARGS__) break;  \
+      case AR_BFLOAT16_ACC32:                                                     \
+        AR_DISPATCH_OPS(FN, AR_BFLOAT16_ACC32, OP, __VA_ARGS__) break;            \
     }                                                                             \
     return hipErrorInvalidValue;                                                  \
   } while (0)

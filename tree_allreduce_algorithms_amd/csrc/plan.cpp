@@ -14,9 +14,14 @@
 
 namespace ar {
 
-size_t itemsize(ar_dtype_t dtype) { return dtype == AR_BFLOAT16 ? 2 : 4; }
+size_t itemsize(ar_dtype_t dtype) {
+  return (dtype == AR_BFLOAT16 || dtype == AR_BFLOAT16_ACC32) ? 2 : 4;
+}
 
-bool dtype_ok(int dtype) { return dtype == AR_INT32 || dtype == AR_FLOAT32 || dtype == AR_BFLOAT16; }
+bool dtype_ok(int dtype) {
+  return dtype == AR_INT32 || dtype == AR_FLOAT32 || dtype == AR_BFLOAT16 ||
+         dtype == AR_BFLOAT16_ACC32;
+}
 
 bool op_ok(int op) { return op == AR_SUM || op == AR_PROD || op == AR_MAX || op == AR_MIN; }
 

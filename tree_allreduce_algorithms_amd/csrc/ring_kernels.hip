@@ -6,6 +6,7 @@
 // up owning chunk r).  Doing those N-1 hops for one element in registers
 // gives bit-for-bit the value the step-by-step ring leaves in rank c; the
 // AllGather pass then only copies it, so AllReduce stores it in every rank.
+// (AR_BFLOAT16_ACC32 runs the same hops on float32 partials and rounds once.)
 #include "device_common.hpp"
 
 namespace ar {
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
     const uint64_t toff = tp * sizeof(P);
     const TileLanes<U, sizeof(P)> ln(tp, s.plo, s.phi);
 
-    P acc[U];
+    using F = Fold<DT, OP, P>;
+    typename F::A acc[U];
     for (int k0 = 0; k0 < n; k0 += B) {
       P in[B][U];
 #pragma unroll
@@ -63,34 +65,39 @@ __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
         if (k0 + j < n) {
 #pragma unroll
           for (int u = 0; u < U; ++u)
-            acc[u] = (k0 + j == 0) ? in[j][u] : combine<DT, OP>(in[j][u], acc[u]);
+            acc[u] = (k0 + j == 0) ? F::widen(in[j][u]) : F::combine(F::widen(in[j][u]), acc[u]);
         }
       }
     }
+    P out[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) out[u] = F::narrow(acc[u]);
     if (ALL) {
       for (int r = 0; r < n; ++r) {
         char* dst = at(a.ptrs.p[r], toff);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (ln.live[u]) store_stream<P>(dst, ln.off[u], acc[u]);
+          if (ln.live[u]) store_stream<P>(dst, ln.off[u], out[u]);
       }
     } else {
       char* dst = at(a.ptrs.p[c], toff);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (ln.live[u]) store_stream<P>(dst, ln.off[u], acc[u]);
+        if (ln.live[u]) store_stream<P>(dst, ln.off[u], out[u]);
     }
   }
 
   if (blockIdx.x == 0 && threadIdx.x < s.scalar_count()) {
+    using FS = Fold<DT, OP, S>;
     const uint64_t e = s.scalar_index(threadIdx.x);
-    S acc = load<S>(a.ptrs.p[first], e);
+    typename FS::A acc = FS::widen(load<S>(a.ptrs.p[first], e));
     for (int k = 1; k < n; ++k)
-      acc = combine<DT, OP>(load<S>(a.ptrs.p[wrap_rank(first + k, n)], e), acc);
+      acc = FS::combine(FS::widen(load<S>(a.ptrs.p[wrap_rank(first + k, n)], e)), acc);
+    const S out = FS::narrow(acc);
     if (ALL) {
-      for (int r = 0; r < n; ++r) store<S>(a.ptrs.p[r], e, acc);
+      for (int r = 0; r < n; ++r) store<S>(a.ptrs.p[r], e, out);
     } else {
-      store<S>(a.ptrs.p[c], e, acc);
+      store<S>(a.ptrs.p[c], e, out);
     }
   }
 }
@@ -123,7 +130,7 @@ hipError_t launch_ring_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtyp
   a.chunk = chunk_size(n, count);
   a.n = n;
   a.tiles = 0;
-  AR_DISPATCH(ring_fold_typed, dtype, op, a, all_ranks, vec, stream);
+  AR_DISPATCH_FOLD(ring_fold_typed, dtype, op, a, all_ranks, vec, stream);
 }
 
 }  // namespace ar

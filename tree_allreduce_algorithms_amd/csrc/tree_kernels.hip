@@ -43,8 +43,10 @@ constexpr int ilog2_ceil(int v) { return v <= 1 ? 0 : 1 + ilog2_ceil((v + 1) / 2
 template <ar_dtype_t DT, ar_op_t OP, int NMAX, int U, class P, class Load>
 __device__ __forceinline__ void tree_fold_values(int n, int tree, int root, const Load& load,
                                                  P out[U]) {
+  using F = Fold<DT, OP, P>;
+  using A = typename F::A;
   constexpr int L = ilog2_ceil(NMAX) + 1;
-  P slot[L][U];
+  A slot[L][U];
 #pragma unroll
   for (int q0 = 0; q0 < NMAX; q0 += kTreeBatch) {
     if (q0 >= n) break;
@@ -62,15 +64,15 @@ __device__ __forceinline__ void tree_fold_values(int n, int tree, int root, cons
     for (int j = 0; j < kTreeBatch; ++j) {
       const int q = q0 + j;   // compile-time after unrolling
       if (q < n) {
-        P cur[U];
+        A cur[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = in[j][u];
+        for (int u = 0; u < U; ++u) cur[u] = F::widen(in[j][u]);
         int l = 0;
 #pragma unroll
         for (int bit = 0; bit < L; ++bit) {
           if (((q >> bit) & 1) == 0) break;
 #pragma unroll
-          for (int u = 0; u < U; ++u) cur[u] = combine<DT, OP>(slot[bit][u], cur[u]);
+          for (int u = 0; u < U; ++u) cur[u] = F::combine(slot[bit][u], cur[u]);
           l = bit + 1;
         }
 #pragma unroll
@@ -82,15 +84,18 @@ __device__ __forceinline__ void tree_fold_values(int n, int tree, int root, cons
       }
     }
   }
+  A res[U];
   bool have = false;
 #pragma unroll
   for (int l = 0; l < L; ++l) {
     if ((n >> l) & 1) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) out[u] = have ? combine<DT, OP>(slot[l][u], out[u]) : slot[l][u];
+      for (int u = 0; u < U; ++u) res[u] = have ? F::combine(slot[l][u], res[u]) : slot[l][u];
       have = true;
     }
   }
+#pragma unroll
+  for (int u = 0; u < U; ++u) out[u] = F::narrow(res[u]);
 }
 
 template <ar_dtype_t DT, ar_op_t OP, int NMAX, bool VEC>
@@ -170,7 +175,7 @@ hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtyp
   a.n = n;
   a.tiles = 0;
   a.root = root;
-  AR_DISPATCH(tree_fold_typed, dtype, op, a, vec, stream);
+  AR_DISPATCH_FOLD(tree_fold_typed, dtype, op, a, vec, stream);
 }
 
 }  // namespace ar
