@@ -230,18 +230,29 @@ def run_one(args):
     # "allreduce" runs the ring or the tree by the library's cost model
     ran = (ar.allreduce_choice(n, t, odt) if args.collective == "allreduce"
            else args.collective)
-    call = {
-        "allreduce": lambda b: ar.allreduce(b, accumulate=acc),
-        "ring_allreduce": lambda b: ar.ring_allreduce(b, accumulate=acc),
-        "tree_allreduce": lambda b: ar.tree_allreduce(b, accumulate=acc),
-        "reduce_scatter": lambda b: ar.reduce_scatter(b, accumulate=acc),
-        "allgather": lambda b: ar.allgather(b),
-        "broadcast": lambda b: ar.broadcast(b, root=args.root),
-        "reduce": lambda b: ar.reduce(b, root=args.root, accumulate=acc),
-        "scatter": lambda b: ar.scatter(b, root=args.root),
-        "gather": lambda b: ar.gather(b, root=args.root),
-        "alltoall": lambda b: ar.alltoall(b),
+    # every call goes through a prepared handle: one library call, arguments
+    # checked once (the host cost of the free functions is paid at setup)
+    method = {
+        "allreduce": lambda rb: rb.allreduce(),
+        "ring_allreduce": lambda rb: rb.ring_allreduce(),
+        "tree_allreduce": lambda rb: rb.tree_allreduce(),
+        "reduce_scatter": lambda rb: rb.reduce_scatter(),
+        "allgather": lambda rb: rb.allgather(),
+        "broadcast": lambda rb: rb.broadcast(root=args.root),
+        "reduce": lambda rb: rb.reduce(root=args.root),
+        "scatter": lambda rb: rb.scatter(root=args.root),
+        "gather": lambda rb: rb.gather(root=args.root),
+        "alltoall": lambda rb: rb.alltoall(),
     }[args.collective]
+    handles = {}
+
+    def call(b):
+        # the entry keeps `b` alive, so its id cannot be reused by another list
+        key = id(b)
+        if key not in handles:
+            handles[key] = (b, ar.RankBuffers(b, accumulate=acc))
+        return method(handles[key][1])
+
     stream = torch.cuda.current_stream(dev)
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_mall else None
 
@@ -340,6 +351,7 @@ def run_one(args):
         del src, dst
 
     del bufs
+    handles.clear()
     torch.cuda.empty_cache()
     if not (args.no_cpu_baseline or args.no_parity):
         print("[bench] checking one call on fresh inputs against the CPU checker",
@@ -350,6 +362,7 @@ def run_one(args):
         torch.cuda.synchronize()
         secs, compared, bad = run_checker(ran, pristine, got, w, args.root, args.cpu_window, odt)
         del pristine, got
+        handles.clear()
         torch.cuda.empty_cache()
         windows = -(-t // args.cpu_window)
         result["parity"] = {"compared_elements": compared, "mismatches": bad,

@@ -668,3 +668,44 @@ def test_accumulate_option_is_validated():
     ar.ring_allreduce(floats, accumulate="float32")       # the buffers' own dtype: the default
     torch.cuda.synchronize()
     assert torch.equal(floats[0], torch.full((16,), 2.0, device=DEV))
+
+
+
+# --- prepared rank sets --------------------------------------------------------------
+
+def test_rank_buffers_match_the_free_functions():
+    """RankBuffers (checked once, one library call per collective) gives the
+    same bits as the free functions, on the current and on another stream."""
+    n, t = 8, 40_000
+    x = workloads.host_inputs(n, t, "bfloat16", "normal", 101, {"std": 1.0})
+    calls = [
+        ("ring_allreduce", lambda rb: rb.ring_allreduce(), lambda b: ar.ring_allreduce(b)),
+        ("reduce_scatter", lambda rb: rb.reduce_scatter(op="max"), lambda b: ar.reduce_scatter(b, op="max")),
+        ("allgather", lambda rb: rb.allgather(), lambda b: ar.allgather(b)),
+        ("broadcast", lambda rb: rb.broadcast(root=5), lambda b: ar.broadcast(b, root=5)),
+        ("tree_allreduce", lambda rb: rb.tree_allreduce(op="min"), lambda b: ar.tree_allreduce(b, op="min")),
+        ("allreduce", lambda rb: rb.allreduce(), lambda b: ar.allreduce(b)),
+        ("reduce", lambda rb: rb.reduce(root=3), lambda b: ar.reduce(b, root=3)),
+        ("scatter", lambda rb: rb.scatter(root=2), lambda b: ar.scatter(b, root=2)),
+        ("gather", lambda rb: rb.gather(root=6), lambda b: ar.gather(b, root=6)),
+        ("alltoall", lambda rb: rb.alltoall(), lambda b: ar.alltoall(b)),
+    ]
+    side = torch.cuda.Stream()
+    for name, prepared, free in calls:
+        a = to_dev(x, "bfloat16")
+        b = to_dev(x, "bfloat16")
+        torch.cuda.synchronize()
+        rb = ar.RankBuffers(a, stream=side)
+        prepared(rb)
+        side.synchronize()
+        free(b)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert torch.equal(a[r].view(torch.int16), b[r].view(torch.int16)), f"{name} rank {r}"
+    acc = to_dev(x, "bfloat16")
+    ar.RankBuffers(acc, accumulate="float32").ring_allreduce()
+    torch.cuda.synchronize()
+    want = oracle.ring_allreduce(x, "sum", "bfloat16_acc32").bufs[0]
+    assert_same(to_host(acc[0], "bfloat16"), want, "bfloat16", "RankBuffers float32 partials")
+    with pytest.raises(ValueError):
+        ar.RankBuffers([torch.zeros(4, device=DEV), torch.zeros(5, device=DEV)])

@@ -8,6 +8,7 @@ it has not been built the call raises.
 
 from .binding import (  # noqa: F401
     ArError,
+    RankBuffers,
     allgather,
     allreduce,
     allreduce_choice,

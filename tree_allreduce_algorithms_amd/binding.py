@@ -92,7 +92,7 @@ def _check(status, where):
 
 
 def _ptr_array(ptrs):
-    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[ctypes.c_void_p(int(p)) for p in ptrs])
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[int(p) for p in ptrs])
     return ctypes.cast(arr, _PP), arr
 
 
@@ -136,14 +136,17 @@ def _prep(tensors):
     if len(tensors) > MAX_RANKS:
         raise ValueError(f"at most {MAX_RANKS} ranks")
     t0 = tensors[0]
+    if not isinstance(t0, torch.Tensor) or not t0.is_cuda:
+        raise TypeError("rank buffers must be GPU tensors")
+    dev, dt, numel = t0.get_device(), t0.dtype, t0.numel()
     for t in tensors:
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError("rank buffers must be GPU tensors")
-        if t.device != t0.device or t.dtype != t0.dtype or t.numel() != t0.numel():
+        if t.get_device() != dev or t.dtype != dt or t.numel() != numel:
             raise ValueError("rank buffers must share device, dtype and size")
         if not t.is_contiguous():
             raise ValueError("rank buffers must be contiguous")
-    return tensors, _torch_dtype_name(t0), t0.numel()
+    return tensors, _torch_dtype_name(t0), numel
 
 
 def _stream_handle(tensors, stream):
@@ -219,6 +222,86 @@ def allreduce(tensors, op="sum", stream=None, accumulate=None):
     """AllReduce in place by the ring or the double tree, whichever the cost
     model predicts faster for this size (see ar_allreduce)."""
     return _collective("allreduce", tensors, op=op, stream=stream, accumulate=accumulate)
+
+
+class RankBuffers:
+    """A fixed set of N rank tensors, checked once.
+
+    Every collective on it is then one call into the library with the
+    pointer array, dtype and stream prepared here, which keeps the host cost
+    of a call to a few microseconds for the small messages where it matters.
+    The object holds references to the tensors; their storage must not be
+    reallocated while it is in use.  ``stream`` (a torch stream or a raw
+    hipStream_t handle) defaults to the current stream at construction; each
+    call may pass another.  ``accumulate='float32'`` (bfloat16 tensors only)
+    selects float32 partials for the reductions.
+    """
+
+    def __init__(self, tensors, stream=None, accumulate=None):
+        self.tensors, dtype, self.count = _prep(tensors)
+        self.n = len(self.tensors)
+        if accumulate not in (None, dtype):
+            if accumulate != "float32" or dtype != "bfloat16":
+                raise ValueError(f"accumulate={accumulate!r} is only offered as 'float32' for "
+                                 f"bfloat16 buffers (got {dtype})")
+        self.dtype = dtype
+        self._copy_dt = DTYPES[dtype]
+        self._red_dt = DTYPES["bfloat16_acc32" if accumulate == "float32" else dtype]
+        self._pp, self._keep = _ptr_array([t.data_ptr() for t in self.tensors])
+        self._stream = _stream_handle(self.tensors, stream)
+        lib_ = lib()
+        self._fn = {name: getattr(lib_, "ar_" + name) for name in COLLECTIVES}
+        self._fn["allreduce"] = lib_.ar_allreduce
+
+    def _s(self, stream):
+        if stream is None:
+            return self._stream
+        return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+    def _run(self, name, status):
+        if status != SUCCESS:
+            raise ArError(status, name)
+        return self.tensors
+
+    def ring_allreduce(self, op="sum", stream=None):
+        return self._run("ring_allreduce", self._fn["ring_allreduce"](
+            self._pp, self.n, self.count, self._red_dt, OPS[op], self._s(stream)))
+
+    def reduce_scatter(self, op="sum", stream=None):
+        return self._run("reduce_scatter", self._fn["reduce_scatter"](
+            self._pp, self.n, self.count, self._red_dt, OPS[op], self._s(stream)))
+
+    def allgather(self, stream=None):
+        return self._run("allgather", self._fn["allgather"](
+            self._pp, self.n, self.count, self._copy_dt, self._s(stream)))
+
+    def broadcast(self, root=0, stream=None):
+        return self._run("broadcast", self._fn["broadcast"](
+            self._pp, self.n, self.count, self._copy_dt, root, self._s(stream)))
+
+    def tree_allreduce(self, op="sum", stream=None):
+        return self._run("tree_allreduce", self._fn["tree_allreduce"](
+            self._pp, self.n, self.count, self._red_dt, OPS[op], self._s(stream)))
+
+    def allreduce(self, op="sum", stream=None):
+        return self._run("allreduce", self._fn["allreduce"](
+            self._pp, self.n, self.count, self._red_dt, OPS[op], self._s(stream)))
+
+    def reduce(self, op="sum", root=0, stream=None):
+        return self._run("reduce", self._fn["reduce"](
+            self._pp, self.n, self.count, self._red_dt, OPS[op], root, self._s(stream)))
+
+    def scatter(self, root=0, stream=None):
+        return self._run("scatter", self._fn["scatter"](
+            self._pp, self.n, self.count, self._copy_dt, root, self._s(stream)))
+
+    def gather(self, root=0, stream=None):
+        return self._run("gather", self._fn["gather"](
+            self._pp, self.n, self.count, self._copy_dt, root, self._s(stream)))
+
+    def alltoall(self, stream=None):
+        return self._run("alltoall", self._fn["alltoall"](
+            self._pp, self.n, self.count, self._copy_dt, self._s(stream)))
 
 
 # --- host-only helpers --------------------------------------------------------
