@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kBlock) void fanout_kernel(FanoutArgs a) {
       char* dp = at(a.ptrs.p[r], toff);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (ln.live[u]) store_stream<P>(dp, ln.off[u], v[u]);
+        if (ln.live[u]) store_cached<P>(dp, ln.off[u], v[u]);
     }
   }
 

@@ -199,7 +199,7 @@ template <class P> __device__ __forceinline__ void store(void* base, uint64_t i,
 // Streaming 16-byte accesses for the pack paths.  A collective touches every
 // byte of every rank buffer once (a read, a write, or a read then a write by
 // the same thread), so there is no reuse for L2 to capture; the non-temporal
-// hint lets the loads and stores stream past it.  Measured on gfx950 with
+// hint lets the loads (and the folds' stores) stream past it.  Measured on gfx950 with
 // 8 x 1.2 GB buffers, the hint raises a pure read stream from about 6.4 to
 // 7.0 TB/s and the 8-rank fold from about 5.2 to 5.5 TB/s.
 using Raw16 = uint32_t __attribute__((ext_vector_type(4)));
@@ -230,6 +230,17 @@ __device__ __forceinline__ void store_stream(char* base, uint32_t off, const P& 
   } else {
     *reinterpret_cast<P*>(base + off) = v;
   }
+}
+
+// Stores that go through the caches.  The copies (the AllGather and Broadcast
+// fan-out, and every step of the literal schedules) write each value they
+// read to one or more other buffers; measured on gfx950 they run faster when
+// their stores are ordinary write-back stores: the fan-out 4-6 % at N = 8
+// and 64, the step AllGather at N = 64 about 30 %.  The folds keep
+// store_stream, whose hint measured 6 % faster for them.
+template <class P>
+__device__ __forceinline__ void store_cached(char* base, uint32_t off, const P& v) {
+  *reinterpret_cast<P*>(base + off) = v;
 }
 
 // Element type T moved either as 16-byte packs (VEC: every rank buffer is

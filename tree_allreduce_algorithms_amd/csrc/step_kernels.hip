@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (ln.live[u])
-        store_stream<P>(dp, ln.off[u], REDUCE ? combine<DT, OP>(own[u], in[u]) : in[u]);
+        store_cached<P>(dp, ln.off[u], REDUCE ? combine<DT, OP>(own[u], in[u]) : in[u]);
   }
 
   if (blockIdx.x == 0 && threadIdx.x < s.scalar_count()) {
