@@ -328,12 +328,15 @@ inline uint64_t tiles_for(uint64_t max_elems, int pack, int unroll) {
   return (packs + per_tile - 1) / per_tile + 1;
 }
 
-// Packs per lane per tile.  Measured on gfx950 with interleaved repeats over
-// 8 x 1.2 GB and 64 x 64 MB rank buffers: the ring fold is best or tied at one
-// pack per lane for every N (each lane already keeps N loads in flight); the
-// fan-out copy is best at four packs for N <= 8 and at two above.  AR_TUNE_UNROLL (1, 2 or 4), read at the first
-// launch, overrides both for measurements; it changes nothing but the pack
-// grouping, never any element's arithmetic.
+// Packs per lane per tile.  Measured on gfx950 by alternating both choices in
+// one process over about 10 GB of rank buffers.  The ring fold is 5 % faster
+// with one pack per lane at N = 4 and 8.  Above N = 8 two packs are faster
+// for the AllReduce at N = 12, 16 and 32 (2-5 %) and tie at N = 64; for the
+// ReduceScatter they are 3.5 % faster at N = 64 and within 2 % at N = 16 and
+// 32.  The fan-out copy is best at four packs for N <= 8 and two above.
+// AR_TUNE_UNROLL (1, 2 or 4), read at the first launch, overrides both for
+// measurements; it changes nothing but the pack grouping, never any element's
+// arithmetic.
 enum class UnrollFor { kFold, kFanout };
 
 inline int pick_unroll(UnrollFor kind, int n) {
@@ -343,7 +346,7 @@ inline int pick_unroll(UnrollFor kind, int n) {
     return (u == 1 || u == 2 || u == 4) ? u : 0;
   }();
   if (forced != 0) return forced;
-  if (kind == UnrollFor::kFold) return 1;
+  if (kind == UnrollFor::kFold) return n <= 8 ? 1 : 2;
   return n <= 8 ? 4 : 2;
 }
 
