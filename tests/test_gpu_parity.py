@@ -709,3 +709,17 @@ def test_rank_buffers_match_the_free_functions():
     assert_same(to_host(acc[0], "bfloat16"), want, "bfloat16", "RankBuffers float32 partials")
     with pytest.raises(ValueError):
         ar.RankBuffers([torch.zeros(4, device=DEV), torch.zeros(5, device=DEV)])
+
+@pytest.mark.parametrize("unroll", ["1", "2", "4"])
+def test_unroll_override_is_bit_identical(unroll):
+    """AR_TUNE_UNROLL only regroups packs: forced to 1, 2 or 4 packs per lane,
+    the fold and fan-out kernels give the oracle's results bit for bit.  The
+    value is read once per process, so each runs in a child process."""
+    import subprocess
+    announce(f"unroll override {unroll} (child process)")
+    env = dict(os.environ, AR_TUNE_UNROLL=unroll)
+    worker = os.path.join(os.path.dirname(os.path.abspath(__file__)), "unroll_worker.py")
+    proc = subprocess.run([sys.executable, "-u", worker], env=env, capture_output=True,
+                          text=True, timeout=110)
+    assert proc.returncode == 0, f"worker failed ({proc.returncode}):\n{proc.stdout[-3000:]}\n{proc.stderr[-3000:]}"
+    assert "all results match" in proc.stdout
