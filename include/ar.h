@@ -30,7 +30,9 @@
  * count   T, elements per rank.  Chunk layout: C = ceil(T/N), chunk c =
  *         [c*C, min(T, (c+1)*C)); only trailing chunks are short, and a chunk
  *         is empty when c*C >= T.  Rank c owns chunk c.
- * stream  a hipStream_t passed as void* (NULL = the null stream).  Calls are
+ * stream  a hipStream_t passed as void* (NULL = the null stream of the
+ *         calling thread's current device, which must then be the device
+ *         that holds the buffers; a non-null stream carries its device).  Calls are
  *         asynchronous and stream-ordered: they enqueue kernels and return;
  *         the library never synchronises.  Completion is observed through
  *         the stream.  All buffers are updated IN PLACE.

@@ -156,6 +156,34 @@ def _stream_handle(tensors, stream):
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+class _on_device:
+    """Makes `dev` the current device for a launch when it is not already.
+
+    The library launches on the stream it is given; the null stream (handle
+    0, torch's default stream) is the current device's, so the tensors'
+    device must be current.  The check costs well under a microsecond when
+    nothing needs to change."""
+
+    __slots__ = ("dev", "prev")
+
+    def __init__(self, dev):
+        self.dev, self.prev = dev, None
+
+    def __enter__(self):
+        import torch
+        cur = torch.cuda.current_device()
+        if cur != self.dev:
+            self.prev = cur
+            torch.cuda.set_device(self.dev)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            import torch
+            torch.cuda.set_device(self.prev)
+        return False
+
+
 def _collective(name, tensors, op=None, root=None, stream=None, accumulate=None):
     tensors, dtype, count = _prep(tensors)
     if accumulate not in (None, dtype):
@@ -163,8 +191,9 @@ def _collective(name, tensors, op=None, root=None, stream=None, accumulate=None)
             raise ValueError(f"accumulate={accumulate!r} is only offered as 'float32' for "
                              f"bfloat16 buffers (got {dtype})")
         dtype = "bfloat16_acc32"
-    status = raw_call(name, [t.data_ptr() for t in tensors], count, dtype, op=op, root=root,
-                      stream=_stream_handle(tensors, stream))
+    with _on_device(tensors[0].get_device()):
+        status = raw_call(name, [t.data_ptr() for t in tensors], count, dtype, op=op,
+                          root=root, stream=_stream_handle(tensors, stream))
     _check(status, name)
     return tensors
 
@@ -233,8 +262,9 @@ class RankBuffers:
     The object holds references to the tensors; their storage must not be
     reallocated while it is in use.  ``stream`` (a torch stream or a raw
     hipStream_t handle) defaults to the current stream at construction; each
-    call may pass another.  ``accumulate='float32'`` (bfloat16 tensors only)
-    selects float32 partials for the reductions.
+    call may pass another.  Calls run with the tensors' device current.
+    ``accumulate='float32'`` (bfloat16 tensors only) selects float32 partials
+    for the reductions.
     """
 
     def __init__(self, tensors, stream=None, accumulate=None):
@@ -249,6 +279,9 @@ class RankBuffers:
         self._red_dt = DTYPES["bfloat16_acc32" if accumulate == "float32" else dtype]
         self._pp, self._keep = _ptr_array([t.data_ptr() for t in self.tensors])
         self._stream = _stream_handle(self.tensors, stream)
+        import torch
+        self._dev = self.tensors[0].get_device()
+        self._current_device = torch.cuda.current_device
         lib_ = lib()
         self._fn = {name: getattr(lib_, "ar_" + name) for name in COLLECTIVES}
         self._fn["allreduce"] = lib_.ar_allreduce
@@ -258,50 +291,46 @@ class RankBuffers:
             return self._stream
         return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
-    def _run(self, name, status):
+    def _call(self, name, *args):
+        fn = self._fn[name]
+        if self._current_device() == self._dev:
+            status = fn(self._pp, self.n, self.count, *args)
+        else:
+            with _on_device(self._dev):
+                status = fn(self._pp, self.n, self.count, *args)
         if status != SUCCESS:
             raise ArError(status, name)
         return self.tensors
 
     def ring_allreduce(self, op="sum", stream=None):
-        return self._run("ring_allreduce", self._fn["ring_allreduce"](
-            self._pp, self.n, self.count, self._red_dt, OPS[op], self._s(stream)))
+        return self._call("ring_allreduce", self._red_dt, OPS[op], self._s(stream))
 
     def reduce_scatter(self, op="sum", stream=None):
-        return self._run("reduce_scatter", self._fn["reduce_scatter"](
-            self._pp, self.n, self.count, self._red_dt, OPS[op], self._s(stream)))
+        return self._call("reduce_scatter", self._red_dt, OPS[op], self._s(stream))
 
     def allgather(self, stream=None):
-        return self._run("allgather", self._fn["allgather"](
-            self._pp, self.n, self.count, self._copy_dt, self._s(stream)))
+        return self._call("allgather", self._copy_dt, self._s(stream))
 
     def broadcast(self, root=0, stream=None):
-        return self._run("broadcast", self._fn["broadcast"](
-            self._pp, self.n, self.count, self._copy_dt, root, self._s(stream)))
+        return self._call("broadcast", self._copy_dt, root, self._s(stream))
 
     def tree_allreduce(self, op="sum", stream=None):
-        return self._run("tree_allreduce", self._fn["tree_allreduce"](
-            self._pp, self.n, self.count, self._red_dt, OPS[op], self._s(stream)))
+        return self._call("tree_allreduce", self._red_dt, OPS[op], self._s(stream))
 
     def allreduce(self, op="sum", stream=None):
-        return self._run("allreduce", self._fn["allreduce"](
-            self._pp, self.n, self.count, self._red_dt, OPS[op], self._s(stream)))
+        return self._call("allreduce", self._red_dt, OPS[op], self._s(stream))
 
     def reduce(self, op="sum", root=0, stream=None):
-        return self._run("reduce", self._fn["reduce"](
-            self._pp, self.n, self.count, self._red_dt, OPS[op], root, self._s(stream)))
+        return self._call("reduce", self._red_dt, OPS[op], root, self._s(stream))
 
     def scatter(self, root=0, stream=None):
-        return self._run("scatter", self._fn["scatter"](
-            self._pp, self.n, self.count, self._copy_dt, root, self._s(stream)))
+        return self._call("scatter", self._copy_dt, root, self._s(stream))
 
     def gather(self, root=0, stream=None):
-        return self._run("gather", self._fn["gather"](
-            self._pp, self.n, self.count, self._copy_dt, root, self._s(stream)))
+        return self._call("gather", self._copy_dt, root, self._s(stream))
 
     def alltoall(self, stream=None):
-        return self._run("alltoall", self._fn["alltoall"](
-            self._pp, self.n, self.count, self._copy_dt, self._s(stream)))
+        return self._call("alltoall", self._copy_dt, self._s(stream))
 
 
 # --- host-only helpers --------------------------------------------------------
