@@ -121,8 +121,10 @@ def traffic_from_profile(workload, collective, impl):
     return int(val.group(1))
 
 
-def algorithmic_bytes(collective, n, t, isz):
+def algorithmic_bytes(collective, n, t, isz, root=0):
     """HBM bytes the fused implementation must move per call."""
+    c = -(-t // n)                                   # chunk size (ragged tail, maybe empty chunks)
+    root_chunk = max(0, min(t, (root + 1) * c) - min(t, root * c))
     return {
         "ring_allreduce": 2 * n * t * isz,     # read N inputs, write N outputs
         "tree_allreduce": 2 * n * t * isz,
@@ -130,22 +132,22 @@ def algorithmic_bytes(collective, n, t, isz):
         "allgather": n * t * isz,              # read each chunk once, write N-1 copies
         "broadcast": n * t * isz,
         "reduce": (n + 1) * t * isz,           # read N, write the root's buffer
-        # one chunk per non-root rank, read once and written once
-        "scatter": 2 * (t - -(-t // n)) * isz if n > 1 else 0,
-        "gather": 2 * (t - -(-t // n)) * isz if n > 1 else 0,
+        # every non-root rank's chunk, read once and written once
+        "scatter": 2 * (t - root_chunk) * isz if n > 1 else 0,
+        "gather": 2 * (t - root_chunk) * isz if n > 1 else 0,
         "alltoall": 2 * (n - 1) * t * isz,     # every off-diagonal block read and written once
     }[collective]
 
 
-def step_bytes(collective, n, t, isz):
+def step_bytes(collective, n, t, isz, root=0):
     """HBM bytes of the literal schedule: 3 per element of a reduce transfer
     (read both sides, write one), 2 per element of a copy transfer."""
     import tree_allreduce_algorithms_amd as ar
-    sent, _ = ar.expected_bytes(collective, n, t, "bfloat16" if isz == 2 else "int32")
+    sent, _ = ar.expected_bytes(collective, n, t, "bfloat16" if isz == 2 else "int32", root=root)
     moved = sum(sent) // isz                     # elements transferred over all steps
     # share of those elements moved by reduce (rather than copy) transfers
     if collective in ("reduce", "alltoall"):     # one implementation
-        return algorithmic_bytes(collective, n, t, isz)
+        return algorithmic_bytes(collective, n, t, isz, root)
     reduce_share = {"ring_allreduce": (1, 2), "tree_allreduce": (1, 2),
                     "reduce_scatter": (1, 1)}.get(collective, (0, 1))
     reduced = moved * reduce_share[0] // reduce_share[1]
@@ -283,13 +285,13 @@ def run_one(args):
 
     launch_ms = sum(event_ms) / len(event_ms)
     per_call_s = (launch_ms * 1e-3) if args.flush_mall else wall / args.steps
-    alg = algorithmic_bytes(ran, n, t, isz)
+    alg = algorithmic_bytes(ran, n, t, isz, args.root)
     # Reduce and AllToAll have one implementation; with float32 partials the
     # reductions run fused under either implementation
     fused = (args.impl == "fused" or ran in ("reduce", "alltoall")
              or (acc is not None and ran in ("ring_allreduce", "reduce_scatter", "tree_allreduce")))
     launches = 1 if fused else ar.expected_steps(ran, n)
-    moved = alg if fused else step_bytes(ran, n, t, isz)
+    moved = alg if fused else step_bytes(ran, n, t, isz, args.root)
     achieved = moved / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(w.name, args.collective, args.impl)
 

@@ -1,0 +1,137 @@
+"""Host-side checks of bench.py (no GPU needed).
+
+* More than one GPU is refused with a message, before any GPU work.
+* The algorithmic HBM bytes the bench divides by kernel time equal what the
+  semantics of each collective force any implementation to move: every input
+  that some defined output depends on must be read once (except a value that
+  simply stays in place), every defined output that differs from its input
+  must be written once.  Both counts are
+  found by perturbing inputs of the oracle on tiny int32 cases.
+* The profile summaries the bench reads parse, and every suite row names a
+  known workload and collective.
+"""
+
+import glob
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from tree_allreduce_algorithms_amd import workloads  # noqa: E402
+
+DT = "int32"
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_is_refused(argv, env):
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
+                          env={**os.environ, **env}, capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "one GPU only" in proc.stderr
+    assert proc.stdout == ""
+
+
+def test_call_count_cap_is_enforced():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "40"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2 and "--warmup + --steps" in proc.stderr
+
+
+def _run(coll, x, root):
+    fn = {
+        "ring_allreduce": lambda: oracle.ring_allreduce(x, "sum", DT),
+        "tree_allreduce": lambda: oracle.tree_allreduce(x, "sum", DT),
+        "reduce_scatter": lambda: oracle.ring_reduce_scatter(x, "sum", DT),
+        "allgather": lambda: oracle.ring_allgather(x, DT),
+        "broadcast": lambda: oracle.broadcast(x, root, DT),
+        "reduce": lambda: oracle.reduce(x, root, "sum", DT),
+        "scatter": lambda: oracle.scatter(x, root, DT),
+        "gather": lambda: oracle.gather(x, root, DT),
+        "alltoall": lambda: oracle.alltoall(x, DT),
+    }[coll]
+    return np.stack(fn().bufs)
+
+
+def _defined(coll, n, t, root):
+    """Mask of the output positions the collective defines (the rest keep
+    unspecified or untouched values)."""
+    owned = oracle.chunk_layout(n, t)
+    m = np.zeros((n, t), dtype=bool)
+    if coll == "reduce_scatter":
+        for r, (lo, hi) in enumerate(owned):
+            m[r, lo:hi] = True
+    elif coll in ("reduce", "gather"):
+        m[root, :] = True
+    elif coll == "scatter":
+        for r, (lo, hi) in enumerate(owned):
+            m[r, lo:hi] = True
+    else:
+        m[:, :] = True
+    return m
+
+
+def _forced_bytes(coll, n, t, root):
+    rng = np.random.default_rng(n * 1000 + t * 10 + root)
+    # wide values, so that no output equals its input by coincidence
+    x = [rng.integers(-(1 << 30), 1 << 30, size=t, dtype=np.int32) for _ in range(n)]
+    base = _run(coll, x, root)
+    defined = _defined(coll, n, t, root)
+    reads = 0
+    for r in range(n):
+        for i in range(t):
+            y = [a.copy() for a in x]
+            y[r][i] += 7
+            changed = (_run(coll, y, root) != base) & defined
+            # an input that only its own position passes through unchanged
+            # (a value that stays where it is) needs no access
+            own_only = changed[r, i] and np.count_nonzero(changed) == 1 and \
+                _run(coll, y, root)[r, i] == y[r][i] and base[r, i] == x[r][i]
+            if np.any(changed) and not own_only:
+                reads += 1
+    writes = int(np.count_nonzero((base != np.stack(x)) & defined))
+    return (reads + writes) * 4
+
+
+CASES = [(2, 5, 0), (3, 7, 2), (4, 10, 1), (4, 4, 3), (5, 13, 4), (5, 3, 4), (5, 11, 0)]
+
+
+@pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce", "reduce_scatter",
+                                  "allgather", "broadcast", "reduce", "scatter", "gather",
+                                  "alltoall"])
+@pytest.mark.parametrize("n,t,root", CASES)
+def test_algorithmic_bytes_are_the_forced_traffic(coll, n, t, root):
+    if coll == "alltoall":
+        t -= t % n
+        if t == 0:
+            pytest.skip("AllToAll needs T >= N")
+    assert bench.algorithmic_bytes(coll, n, t, 4, root) == _forced_bytes(coll, n, t, root)
+
+
+def test_profile_summaries_parse():
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md")))
+    assert paths, "no traffic summaries committed"
+    for p in paths:
+        text = open(p).read()
+        assert re.search(r"^kernel_source_sha256:\s*[0-9a-f]{64}\s*$", text, re.M), p
+        m = re.search(r"^hbm_bytes_per_launch:\s*(\d+)\s*$", text, re.M)
+        assert m and int(m.group(1)) > 0, p
+    trace = glob.glob(os.path.join(ROOT, "profiles", "*_trace.md"))
+    assert trace, "no kernel-trace summary committed"
+
+
+def test_suite_rows_are_valid():
+    for wname, coll, impl, extra in bench.SUITE:
+        assert wname in workloads.WORKLOADS, wname
+        assert coll in bench.COLLECTIVES, coll
+        assert impl in ("fused", "step")
+        args = bench.parse(["--workload", wname, "--collective", coll, "--impl", impl] + extra)
+        assert args.warmup + args.steps <= bench.MAX_CALLS
