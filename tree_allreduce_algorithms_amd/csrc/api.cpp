@@ -34,26 +34,26 @@ thread_local int t_last_hip_error = 0;
 // Cost model coefficients (alpha_us per launch, gbps of HBM traffic) per
 // collective and implementation.  The AllReduce pairs are the least-squares
 // fit of launches * alpha + bytes / gbps to the N=4 float32 message-size sweep
-// (1 KiB to 256 MiB per rank, Infinity Cache flushed before every call) on one
-// MI355X.  ReduceScatter, AllGather and Broadcast were measured at one size
-// (N=64, 64 MB per rank), which fixes their bandwidth; they take the
-// AllReduce fit's per-launch alpha.  Reduce runs the tree fold kernel and
-// Scatter / Gather one copy step, so they take those kernels' coefficients.
+// (1 KiB to 256 MiB per rank, Infinity Cache flushed before every call), two
+// runs on two MI355X boxes pooled.  The other collectives were measured at
+// one size each (N=64 x 64 MB per rank; AllToAll N=8 x 128 MiB), which fixes
+// their bandwidth given the AllReduce fit's per-launch alpha (the tree fold's
+// for Reduce, a step launch's for Scatter, Gather and AllToAll).
 struct CostCoeff {
   double alpha_us;
   double gbps;
 };
 std::mutex g_cost_mu;
 CostCoeff g_cost[9][2] = {
-    {{6.18, 5905.0}, {3.16, 6186.0}},   // ring AllReduce: fused, step
-    {{6.18, 5721.0}, {3.16, 5243.0}},   // ReduceScatter
-    {{6.18, 4940.0}, {3.16, 4609.0}},   // AllGather
-    {{6.18, 5052.0}, {3.16, 5790.0}},   // Broadcast
-    {{6.21, 5825.0}, {3.24, 6090.0}},   // double-tree AllReduce
-    {{6.21, 5825.0}, {6.21, 5825.0}},   // Reduce (fused either way)
-    {{3.16, 5790.0}, {3.16, 5790.0}},   // Scatter (one step either way)
-    {{3.16, 5790.0}, {3.16, 5790.0}},   // Gather (one step either way)
-    {{3.16, 5790.0}, {3.16, 5790.0}},   // AllToAll (one kernel either way)
+    {{6.36, 5823.0}, {3.44, 6635.0}},   // ring AllReduce: fused, step
+    {{6.36, 5956.0}, {3.44, 6548.0}},   // ReduceScatter
+    {{6.36, 5287.0}, {3.44, 7327.0}},   // AllGather
+    {{6.36, 5284.0}, {3.44, 5777.0}},   // Broadcast
+    {{5.85, 5764.0}, {3.19, 6030.0}},   // double-tree AllReduce
+    {{5.85, 5827.0}, {5.85, 5827.0}},   // Reduce (fused either way)
+    {{3.44, 5049.0}, {3.44, 5049.0}},   // Scatter (one step either way)
+    {{3.44, 5014.0}, {3.44, 5014.0}},   // Gather (one step either way)
+    {{3.44, 5845.0}, {3.44, 5845.0}},   // AllToAll (one kernel either way)
 };
 
 bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_ALLTOALL; }
