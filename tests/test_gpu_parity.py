@@ -723,3 +723,70 @@ def test_unroll_override_is_bit_identical(unroll):
                           text=True, timeout=110)
     assert proc.returncode == 0, f"worker failed ({proc.returncode}):\n{proc.stdout[-3000:]}\n{proc.stderr[-3000:]}"
     assert "all results match" in proc.stdout
+
+
+# --- randomized cases ----------------------------------------------------------
+
+def _random_case(case_id):
+    """Case `case_id` of a fixed, seeded draw: any collective and
+    implementation, dtype (bfloat16 with float32 partials included), op,
+    root, N and T, 16-byte or element-aligned buffers."""
+    rng = np.random.default_rng(1_000_003 + case_id)
+    coll = sorted(CALLS)[rng.integers(len(CALLS))]
+    acc32 = coll in ACC32_CALLS and rng.random() < 0.25
+    dtype = "bfloat16" if acc32 else ("int32", "float32", "bfloat16")[rng.integers(3)]
+    n = int(rng.integers(1, 10)) if rng.random() < 0.5 else int(rng.choice([12, 16, 31, 33, 63, 64]))
+    t = int(rng.integers(0, 41)) if rng.random() < 0.3 else int(np.exp(rng.uniform(np.log(41), np.log(100_000))))
+    op = "sum" if coll in NO_OP else ("sum", "prod", "max", "min")[rng.integers(4)]
+    root = int(rng.integers(n))
+    impl = IMPLS[rng.integers(2)]
+    offsets = [int(o) for o in rng.integers(0, 4, size=n)] if rng.random() < 0.4 else None
+    return coll, acc32, dtype, n, t, op, root, impl, offsets, int(rng.integers(100_000))
+
+
+@pytest.mark.parametrize("case_id", range(60))
+def test_randomized_cases_match_oracle(case_id):
+    """Seeded random problems: N from 1 to 64, T from 0 to 100,000 (ragged,
+    below N, empty), every collective, implementation, dtype, op and root,
+    with 16-byte or element-aligned buffers.  Every defined output element
+    must equal the oracle's bit for bit, and nothing outside the buffers may
+    change."""
+    coll, acc32, dtype, n, t, op, root, impl, offsets, seed = _random_case(case_id)
+    dist = "int_uniform" if dtype == "int32" else "normal"
+    x = fit_inputs(coll, workloads.host_inputs(n, t, dtype, dist, seed, _params(dist, n)))
+    t = len(x[0])
+    announce(f"random case {case_id}: {coll} acc32={acc32} impl={impl} n={n} t={t} dtype={dtype} "
+             f"op={op} root={root} offsets={offsets}")
+    if acc32:
+        run, want = ACC32_CALLS[coll][0], ACC32_CALLS[coll][1](x, op, root).bufs
+    else:
+        run, want = CALLS[coll][0], CALLS[coll][1](x, op, dtype, root).bufs
+    ar.set_impl(impl)
+    try:
+        if offsets is None:
+            base, views = None, to_dev(x, dtype)
+        else:
+            base, views = _element_aligned_views(n, t, dtype, offsets)
+            for v, s_ in zip(views, to_dev(x, dtype)):
+                v.copy_(s_)
+            outside = base.clone()
+            for v in views:
+                outside[v.storage_offset(): v.storage_offset() + t] = 0
+        run(views, op, root)
+        torch.cuda.synchronize()
+    finally:
+        ar.set_impl("fused")
+    owned = oracle.chunk_layout(n, t)
+    for r in range(n):
+        got = to_host(views[r], dtype)
+        if coll == "reduce_scatter":
+            lo, hi = owned[r]
+            assert_same(got[lo:hi], want[r][lo:hi], dtype, f"{coll} rank {r}")
+        else:
+            assert_same(got, want[r], dtype, f"{coll} rank {r}")
+    if base is not None:
+        after = base.clone()
+        for v in views:
+            after[v.storage_offset(): v.storage_offset() + t] = 0
+        view16 = (lambda a: a.view(torch.int16)) if dtype == "bfloat16" else (lambda a: a)
+        assert torch.equal(view16(after), view16(outside))
