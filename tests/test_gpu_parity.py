@@ -255,6 +255,45 @@ def test_allgather_after_reduce_scatter_equals_allreduce(dtype):
     ar.set_impl("fused")
 
 
+def test_concurrent_streams_keep_their_own_order():
+    """Two independent rank-buffer sets reduced on two streams at the same
+    time, several calls each, interleaved on the host (as overlapped gradient
+    buckets would be): each set ends exactly as the oracle's same sequence of
+    calls leaves it, so neither stream's kernels see the other's data."""
+    sets = [(8, 300_007, "float32", 61), (5, 200_003, "bfloat16", 62)]
+    xs = [workloads.host_inputs(n, t, dt, "normal", seed, {"std": 1.0}) for n, t, dt, seed in sets]
+    wants = []
+    for (n, t, dt, _), x in zip(sets, xs):
+        # calls that do not commute: Gather picks up rank 0's chunk after the
+        # Reduce has changed it, and the AllReduce sees the gathered root
+        w = oracle.reduce(x, 0, "sum", dt).bufs               # call 1: Reduce to rank 0
+        w = oracle.gather(w, n - 1, dt).bufs                  # call 2: Gather to the last rank
+        w = oracle.tree_allreduce(w, "max", dt).bufs          # call 3: tree AllReduce (max)
+        w = oracle.ring_reduce_scatter(w, "sum", dt).bufs     # call 4: ReduceScatter
+        wants.append(w)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    handles = []
+    for (n, t, dt, _), x, st_ in zip(sets, xs, streams):
+        handles.append(ar.RankBuffers(to_dev(x, dt), stream=st_))
+    torch.cuda.synchronize()
+    announce("two streams, interleaved calls")
+    for h in handles:
+        h.reduce(root=0)
+    for h, (n, _, _, _) in zip(handles, sets):
+        h.gather(root=n - 1)
+    for h in handles:
+        h.tree_allreduce(op="max")
+    for h in handles:
+        h.reduce_scatter()
+    for st_ in streams:
+        st_.synchronize()
+    for h, (n, t, dt, _), w in zip(handles, sets, wants):
+        owned = oracle.chunk_layout(n, t)
+        for r in range(n):
+            lo, hi = owned[r]
+            assert_same(to_host(h.tensors[r], dt)[lo:hi], w[r][lo:hi], dt, f"{dt} rank {r}")
+
+
 def test_non_default_stream():
     n, t = 4, 65_537
     x = workloads.host_inputs(n, t, "float32", "normal", 41, {"std": 1.0})
