@@ -107,15 +107,17 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def traffic_from_profile(workload, collective, impl):
-    """HBM bytes per launch from the committed PMC summary of this kernel and
+def traffic_from_profile(workload, collective, impl, per_call=False):
+    """HBM bytes per launch (per call for a multi-launch implementation, with
+    per_call) from the committed PMC summary of this implementation and
     workload, if it was taken on the current kernel source; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{collective}_{impl}_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
+    key = "hbm_bytes_per_call" if per_call else "hbm_bytes_per_launch"
     sha = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
-    val = re.search(r"^hbm_bytes_per_launch:\s*([0-9]+)\s*$", text, re.M)
+    val = re.search(rf"^{key}:\s*([0-9]+)\s*$", text, re.M)
     if not sha or not val or sha.group(1) != kernel_source_hash():
         return None
     return int(val.group(1))
@@ -293,7 +295,7 @@ def run_one(args):
     launches = 1 if fused else ar.expected_steps(ran, n)
     moved = alg if fused else step_bytes(ran, n, t, isz, args.root)
     achieved = moved / (launch_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(w.name, args.collective, args.impl)
+    traffic = traffic_from_profile(w.name, args.collective, args.impl, per_call=launches > 1)
 
     result = {
         "metric": METRIC,

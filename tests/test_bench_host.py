@@ -122,10 +122,21 @@ def test_profile_summaries_parse():
     for p in paths:
         text = open(p).read()
         assert re.search(r"^kernel_source_sha256:\s*[0-9a-f]{64}\s*$", text, re.M), p
-        m = re.search(r"^hbm_bytes_per_launch:\s*(\d+)\s*$", text, re.M)
-        assert m and int(m.group(1)) > 0, p
+        m = re.search(r"^hbm_bytes_per_(launch|call):\s*(\d+)\s*$", text, re.M)
+        assert m and int(m.group(2)) > 0, p
     trace = glob.glob(os.path.join(ROOT, "profiles", "*_trace.md"))
     assert trace, "no kernel-trace summary committed"
+
+
+def test_traffic_lookup_reads_the_matching_key():
+    """A single-launch line reads bytes per launch, a multi-launch (step)
+    line bytes per call; a missing profile gives None."""
+    if bench.traffic_from_profile("large_grad_fp32", "ring_allreduce", "fused") is not None:
+        assert bench.traffic_from_profile("large_grad_fp32", "ring_allreduce", "fused",
+                                          per_call=True) is None
+    if bench.traffic_from_profile("large_grad_fp32", "ring_allreduce", "step", per_call=True):
+        assert bench.traffic_from_profile("large_grad_fp32", "ring_allreduce", "step") is None
+    assert bench.traffic_from_profile("no_such_workload", "ring_allreduce", "fused") is None
 
 
 def test_suite_rows_are_valid():
