@@ -211,8 +211,27 @@ def test_signed_zero_nan_and_infinity_rules():
         for coll in ("ring_allreduce", "tree_allreduce"):
             compare_collective(coll, x, "float32", op, 0)
     xb = [oracle.f32_to_bf16_rne(a) for a in x]
-    for op in ("max", "min", "sum"):
-        compare_collective("ring_allreduce", xb, "bfloat16", op, 0)
+    for op in ("max", "min", "sum", "prod"):
+        for coll in ("ring_allreduce", "tree_allreduce"):
+            compare_collective(coll, xb, "bfloat16", op, 0)
+    # the same rules with float32 partials: the hops are float32 operations
+    # (NaN, infinities and signed zeros as in float32), rounded once
+    for op in ("max", "min", "sum", "prod"):
+        for coll in sorted(ACC32_CALLS):
+            announce(f"special values, float32 partials: {coll} op={op}")
+            want = ACC32_CALLS[coll][1](xb, op, 2).bufs
+            bufs = to_dev(xb, "bfloat16")
+            ACC32_CALLS[coll][0](bufs, op, 2)
+            torch.cuda.synchronize()
+            owned = oracle.chunk_layout(len(xb), len(xb[0]))
+            for r in range(len(xb)):
+                got = to_host(bufs[r], "bfloat16")
+                if coll == "reduce_scatter":
+                    lo, hi = owned[r]
+                    got, w_ = got[lo:hi], want[r][lo:hi]
+                else:
+                    w_ = want[r]
+                assert_same(got, w_, "bfloat16", f"acc32 {coll} {op} rank {r}")
 
 
 def test_int32_wraparound():
