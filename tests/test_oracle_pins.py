@@ -389,6 +389,30 @@ def test_reduce_fold_order_closed_form(n, t, dtype):
         np.testing.assert_array_equal(oracle.reduce(x, root, "sum", dtype).bufs[root], want)
 
 
+@pytest.mark.parametrize("n,t", FP_SHAPES)
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_double_tree_fold_order_closed_form(n, t, dtype):
+    """The double tree (Lecture 09, section 5.2; Chapter 4, section 4.3.2) as
+    the binomial recursion on each half: elements [0, ceil(T/2)) fold roles
+    = ranks, the rest fold the mirrored roles N-1-rank; every hop is one
+    operation in the dtype (per-hop rounding for bfloat16, through torch)."""
+    x = _normals(n, t, 9000 + n * t, dtype)
+    if dtype == "float32":
+        add = lambda a, b: a + b
+    else:
+        def add(a, b):
+            widen = lambda u: torch.from_numpy(u.view(np.int16).copy()).view(torch.bfloat16).float()
+            s_ = (widen(a) + widen(b)).to(torch.bfloat16)
+            return s_.view(torch.int16).numpy().view(np.uint16)
+    h = -(-t // 2)
+    want = np.empty(t, dtype=x[0].dtype)
+    want[:h] = _binomial_fold_closed_form([v[:h] for v in x], add)
+    want[h:] = _binomial_fold_closed_form([x[n - 1 - q][h:] for q in range(n)], add)
+    res = oracle.tree_allreduce(x, "sum", dtype)
+    for r in range(n):
+        np.testing.assert_array_equal(res.bufs[r], want)
+
+
 @pytest.mark.parametrize("n,t", SHAPES)
 def test_scatter_and_gather_brute_force(n, t):
     x = _ints(n, t, 9 * n + t)
