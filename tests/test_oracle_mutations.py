@@ -52,6 +52,25 @@ def _pins_hold():
         bc = oracle.broadcast(x, root, "int32")
         if any(not np.array_equal(b, x[root]) for b in bc.bufs) or int(bc.recv[root]) != 0:
             return False
+    # double-tree order on an odd T: the binomial recursion on each half
+    # (roles = ranks below ceil(T/2), mirrored roles above)
+    rng = np.random.default_rng(77)
+    for n, t in [(5, 11), (8, 9)]:
+        x = [rng.standard_normal(t).astype(np.float32) for _ in range(n)]
+
+        def fold(vals):
+            def block(q, k):
+                if k == 0:
+                    return vals[q]
+                half = 1 << (k - 1)
+                low = block(q, k - 1)
+                return low + block(q + half, k - 1) if q + half < len(vals) else low
+            return block(0, oracle.ceil_log2(len(vals)))
+
+        h = -(-t // 2)
+        want = np.concatenate([fold([v[:h] for v in x]), fold([x[n - 1 - q][h:] for q in range(n)])])
+        if any(not np.array_equal(b, want) for b in oracle.tree_allreduce(x, "sum", "float32").bufs):
+            return False
     with open(os.path.join(GOLDEN, "order_examples.json")) as f:
         for case in json.load(f)["cases"]:
             x = [np.array(v, dtype=np.float32) for v in case["inputs"]]
@@ -74,6 +93,9 @@ MUTATIONS = {
     "ring_skips_a_neighbour": ("ring_next", lambda r, n: (r + 2) % n),
     "ring_turns_left": ("ring_next", lambda r, n: (r - 1) % n),
     "tree_one_not_mirrored": ("tree_rank", lambda tree, role, n: role),
+    "double_tree_split_at_floor": (
+        "_tree_segments",
+        lambda trees, total: [(0, 0, total)] if trees == 1 else [(0, 0, total // 2), (1, total // 2, total)]),
     "rooted_tree_ignores_root": ("rooted_rank", lambda role, root, n: role),
     "alltoall_keeps_block_index": ("alltoall_slot", lambda src, dst: dst),
     "receiver_overwrites_instead_of_adding": (
