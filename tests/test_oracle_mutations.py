@@ -112,3 +112,55 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(oc, attr, fn)
     assert not _pins_hold(), f"mutation {name} survived every pin"
+
+
+# --- bfloat16 rounding: a wrong rounding rule must fail the rounding pins ------
+
+def _truncate(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _half_up(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x8000) >> 16).astype(np.uint16)
+
+
+def _half_odd(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    odd = (u >> 16) & 1
+    return ((u + 0x7FFF + (1 - odd)) >> 16).astype(np.uint16)
+
+
+def _bf16_pins_hold():
+    """The rounding golden cases (tests/golden/bf16_rounding.json, IEEE ties)
+    and a bfloat16 per-hop AllReduce whose partials hit ties."""
+    with open(os.path.join(GOLDEN, "bf16_rounding.json")) as f:
+        cases = json.load(f)["cases"]
+    bits = np.array([int(c["f32_bits"], 16) for c in cases], dtype=np.uint32)
+    want = np.array([int(c["bf16_bits"], 16) for c in cases], dtype=np.uint16)
+    if not np.array_equal(oracle.f32_to_bf16_rne(bits.view(np.float32)), want):
+        return False
+    # A per-hop bfloat16 AllReduce whose partials land on ties.  N = 3, T = 3
+    # (one element per chunk); rank 0 holds 1 + 2^-7, ranks 1 and 2 hold 2^-8.
+    # Chunk 0 folds ranks 1, 2, 0: 2^-8 + 2^-8 = 2^-7, then 1 + 2^-6, exact.
+    # Chunk 1 folds ranks 2, 0, 1: (1 + 2^-7) + 2^-8 = 1 + 3*2^-8 is a tie that
+    # rounds up to 1 + 2^-6 (even mantissa 0000010), then + 2^-8 = 1 + 5*2^-8,
+    # a tie that rounds down to 1 + 2^-6.  Chunk 2 folds ranks 0, 1, 2: the
+    # same two ties.  With ties to even every rank ends with 1 + 2^-6 (0x3F82)
+    # everywhere; truncation, half-up and half-to-odd each give another value.
+    x = [np.full(3, 0x3F81, np.uint16), np.full(3, 0x3B80, np.uint16), np.full(3, 0x3B80, np.uint16)]
+    res = oracle.ring_allreduce(x, "sum", "bfloat16")
+    return all(np.array_equal(b, np.full(3, 0x3F82, np.uint16)) for b in res.bufs)
+
+
+def test_unmutated_rounding_passes():
+    assert _bf16_pins_hold()
+
+
+@pytest.mark.parametrize("rule", [_truncate, _half_up, _half_odd], ids=["truncate", "half_up", "half_to_odd"])
+def test_wrong_bf16_rounding_is_caught(rule, monkeypatch):
+    import oracle.numerics as on
+    monkeypatch.setattr(on, "f32_to_bf16_rne", rule)
+    monkeypatch.setattr(oracle, "f32_to_bf16_rne", rule)
+    assert not _bf16_pins_hold(), f"rounding rule {rule.__name__} survived the pins"
