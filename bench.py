@@ -107,11 +107,13 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def traffic_from_profile(workload, collective, impl, per_call=False):
+def traffic_from_profile(workload, collective, impl, per_call=False, accumulate=None):
     """HBM bytes per launch (per call for a multi-launch implementation, with
     per_call) from the committed PMC summary of this implementation and
-    workload, if it was taken on the current kernel source; None otherwise."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{collective}_{impl}_{workload}.md")
+    workload (and accumulator: bfloat16 with float32 partials is a kernel of
+    its own), if it was taken on the current kernel source; None otherwise."""
+    suffix = "_float32_partials" if accumulate else ""
+    path = os.path.join(ROOT, "profiles", f"traffic_{collective}_{impl}_{workload}{suffix}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -295,7 +297,8 @@ def run_one(args):
     launches = 1 if fused else ar.expected_steps(ran, n)
     moved = alg if fused else step_bytes(ran, n, t, isz, args.root)
     achieved = moved / (launch_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(w.name, args.collective, args.impl, per_call=launches > 1)
+    traffic = traffic_from_profile(w.name, args.collective, args.impl, per_call=launches > 1,
+                                   accumulate=acc)
 
     result = {
         "metric": METRIC,

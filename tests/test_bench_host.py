@@ -137,6 +137,12 @@ def test_traffic_lookup_reads_the_matching_key():
     if bench.traffic_from_profile("large_grad_fp32", "ring_allreduce", "step", per_call=True):
         assert bench.traffic_from_profile("large_grad_fp32", "ring_allreduce", "step") is None
     assert bench.traffic_from_profile("no_such_workload", "ring_allreduce", "fused") is None
+    # bfloat16 with float32 partials is a kernel of its own, with a summary of its own
+    hop = bench.traffic_from_profile("large_grad_bf16", "ring_allreduce", "fused")
+    acc = bench.traffic_from_profile("large_grad_bf16", "ring_allreduce", "fused",
+                                     accumulate="float32")
+    if hop is not None and acc is not None:
+        assert hop != acc
 
 
 def test_suite_rows_are_valid():
