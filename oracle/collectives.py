@@ -15,9 +15,10 @@ Conventions shared by every function here:
   ring -- and Lecture 09's lab 1 demands that N divide T).  Where N does not
   divide T this oracle takes C = ceil(T/N) and chunk c = [c*C, min(T,(c+1)*C)),
   so only trailing chunks are short and a chunk may be empty when T < N.
-* A "send" is a copy of the sender's chunk taken for every rank before any
-  receive of that step is applied, exactly like the per-step packet snapshot
-  of Lecture 09's lab 1.
+* A step is a map from the state before it to the state after it: what every
+  rank receives in a step is read from the state before that step, and only
+  then do the receivers update their buffers (in a real ring all ranks send
+  and receive at once).
 * Byte counters count logical inter-rank bytes: every transfer of k elements
   adds k*itemsize to the sender's ``sent`` and the receiver's ``recv``.
 * Windowed runs: every element's result depends only on the N values at its
@@ -152,32 +153,38 @@ def _float32_partials(x, run):
 
 # --- ring --------------------------------------------------------------------
 
-def _ring_reduce_scatter_steps(bufs, sent, recv, span, op, dtype):
+def _ring_pass(bufs, sent, recv, span, dtype, steps, chunk_sent, merge):
+    """Run ``steps`` ring steps.  One step maps the state before it to the
+    state after it: rank d's inbox is filled from the pre-step state, with the
+    chunk ``chunk_sent(r, t, n)`` of every rank r whose ring successor is d
+    (exactly one on a ring), and only then does every rank merge its inbox
+    into its own buffer at that chunk: ``merge(own, incoming)``."""
     n = len(bufs)
-    for t in range(n - 1):
-        packets = []
-        for r in range(n):
-            c = rs_send_chunk(r, t, n)
-            packets.append((r, c, bufs[r][span[c]].copy()))
-        for r, c, payload in packets:
-            d = ring_next(r, n)
-            bufs[d][span[c]] = combine(bufs[d][span[c]], payload, op, dtype)
-            _count(sent, recv, r, d, payload.size, dtype)
-    return n - 1 if n > 1 else 0
+    senders = [[r for r in range(n) if ring_next(r, n) == d] for d in range(n)]
+    for t in range(steps):
+        inbox = [[(r, chunk_sent(r, t, n)) for r in senders[d]] for d in range(n)]
+        inbox = [[(r, c, bufs[r][span[c]].copy()) for r, c in box] for box in inbox]
+        for d, box in enumerate(inbox):
+            for r, c, incoming in box:
+                bufs[d][span[c]] = merge(bufs[d][span[c]], incoming)
+                _count(sent, recv, r, d, incoming.size, dtype)
+    return steps
+
+
+def _ring_reduce_scatter_steps(bufs, sent, recv, span, op, dtype):
+    """N-1 steps; the receiver stores own (+) incoming (Lecture 09 section
+    4.3; Chapter 4 section 4.3.1)."""
+    steps = len(bufs) - 1 if len(bufs) > 1 else 0
+    return _ring_pass(bufs, sent, recv, span, dtype, steps, rs_send_chunk,
+                      lambda own, incoming: combine(own, incoming, op, dtype))
 
 
 def _ring_allgather_steps(bufs, sent, recv, span, dtype):
-    n = len(bufs)
-    for t in range(n - 1):
-        packets = []
-        for r in range(n):
-            c = ag_send_chunk(r, t, n)
-            packets.append((r, c, bufs[r][span[c]].copy()))
-        for r, c, payload in packets:
-            d = ring_next(r, n)
-            bufs[d][span[c]] = payload
-            _count(sent, recv, r, d, payload.size, dtype)
-    return n - 1 if n > 1 else 0
+    """N-1 steps; the receiver overwrites its copy of the chunk (Lecture 09
+    section 4.3)."""
+    steps = len(bufs) - 1 if len(bufs) > 1 else 0
+    return _ring_pass(bufs, sent, recv, span, dtype, steps, ag_send_chunk,
+                      lambda own, incoming: incoming)
 
 
 def _ring_spans(n, total, window_start, length):

@@ -164,3 +164,102 @@ def test_wrong_bf16_rounding_is_caught(rule, monkeypatch):
     monkeypatch.setattr(on, "f32_to_bf16_rne", rule)
     monkeypatch.setattr(oracle, "f32_to_bf16_rne", rule)
     assert not _bf16_pins_hold(), f"rounding rule {rule.__name__} survived the pins"
+
+
+# --- PROD / MAX / MIN on float32 and bfloat16: planted operator mistakes ---------
+
+import oracle.numerics as on  # noqa: E402
+
+_COMBINE = on.combine
+
+
+def _op_pins_hold():
+    """A compact run of the operator pins of test_oracle_ops.py: MAX/MIN brute
+    force over the rank axis (float32, bfloat16), the ring and tree PROD fold
+    closed forms (float32, per-hop bfloat16), and the hand-derived op goldens."""
+    import test_oracle_ops as ops
+    with np.errstate(over="ignore"):
+        for dtype in ("float32", "bfloat16"):
+            for n, t in [(4, 64), (5, 23), (8, 40)]:
+                for op in ("max", "min"):
+                    x = ops._signed_values(n, t, 7 * n + t, dtype)
+                    want = ops._extreme(x, op, dtype)
+                    for res in (oracle.ring_allreduce(x, op, dtype), oracle.tree_allreduce(x, op, dtype)):
+                        if any(not np.array_equal(b.view(np.uint8), want.view(np.uint8)) for b in res.bufs):
+                            return False
+                x = ops._near_one(n, t, 11 * n + t, dtype)
+                wide = [a if dtype == "float32" else ops._torch_widen(a) for a in x]
+                want = ops._to_storage(ops._ring_prod_closed_form(wide, ops._mul(dtype)), dtype)
+                if any(not np.array_equal(b, want) for b in oracle.ring_allreduce(x, "prod", dtype).bufs):
+                    return False
+        for case in ops._load_op_examples():
+            x = ops._bits(case["inputs_bits"], case["dtype"])
+            fn = oracle.ring_allreduce if case["collective"] == "ring_allreduce" else oracle.tree_allreduce
+            res = fn(x, case["op"], case["dtype"])
+            for b, want in zip(res.bufs, ops._bits(case["expected_bits"], case["dtype"])):
+                if not np.array_equal(b.view(np.uint8), want.view(np.uint8)):
+                    return False
+    return True
+
+
+def _swap_max_min(local, incoming, op, dtype):
+    if dtype == "float32" and op in ("max", "min"):
+        op = "min" if op == "max" else "max"
+    return _COMBINE(local, incoming, op, dtype)
+
+
+def _bf16_max_on_raw_bits(local, incoming, op, dtype):
+    if dtype == "bfloat16" and op == "max":
+        a = np.asarray(local, dtype=np.uint16)
+        b = np.asarray(incoming, dtype=np.uint16)
+        return np.where(b > a, b, a).astype(np.uint16)
+    return _COMBINE(local, incoming, op, dtype)
+
+
+def _f32_prod_as_sum(local, incoming, op, dtype):
+    if dtype == "float32" and op == "prod":
+        return _COMBINE(local, incoming, "sum", dtype)
+    return _COMBINE(local, incoming, op, dtype)
+
+
+def _bf16_min_on_raw_bits(local, incoming, op, dtype):
+    if dtype == "bfloat16" and op == "min":
+        a = np.asarray(local, dtype=np.uint16)
+        b = np.asarray(incoming, dtype=np.uint16)
+        return np.where(b < a, b, a).astype(np.uint16)
+    return _COMBINE(local, incoming, op, dtype)
+
+
+def _max_takes_incoming_on_ties(local, incoming, op, dtype):
+    if dtype == "float32" and op == "max":
+        a = np.asarray(local, dtype=np.float32)
+        b = np.asarray(incoming, dtype=np.float32)
+        return np.where(b >= a, b, a).astype(np.float32)
+    return _COMBINE(local, incoming, op, dtype)
+
+
+def _bf16_prod_truncates(local, incoming, op, dtype):
+    if dtype == "bfloat16" and op == "prod":
+        prod = on.bf16_to_f32(local) * on.bf16_to_f32(incoming)
+        return (np.ascontiguousarray(prod, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return _COMBINE(local, incoming, op, dtype)
+
+
+OP_MUTATIONS = {
+    "float32_max_min_swapped": _swap_max_min,
+    "bfloat16_max_on_raw_bits": _bf16_max_on_raw_bits,
+    "bfloat16_min_on_raw_bits": _bf16_min_on_raw_bits,
+    "float32_prod_as_sum": _f32_prod_as_sum,
+    "float32_max_takes_incoming_on_ties": _max_takes_incoming_on_ties,
+    "bfloat16_prod_truncates": _bf16_prod_truncates,
+}
+
+
+def test_unmutated_operators_pass():
+    assert _op_pins_hold()
+
+
+@pytest.mark.parametrize("name", sorted(OP_MUTATIONS))
+def test_planted_operator_mistake_is_caught(name, monkeypatch):
+    monkeypatch.setattr(oc, "combine", OP_MUTATIONS[name])
+    assert not _op_pins_hold(), f"mutation {name} survived the operator pins"
