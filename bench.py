@@ -25,10 +25,14 @@ every output written once) over its average event-timed duration, against the
 FETCH_SIZE / WRITE_SIZE counters measured for the same kernel source (from the
 committed summary under profiles/), else null.
 
-After timing, one more call runs on freshly drawn inputs and its whole output
-is compared, window by window, with the CPU checker (a literal NumPy
-simulation of the schedule, single-threaded) on the same inputs; the
-checker's time over all windows is the cpu_baseline.  With --flush-mall a
+After timing, one more call runs on freshly drawn inputs.  The library's
+per-rank byte counters for that call go into the line next to their closed
+forms (for the ring AllReduce: 2 T (N-1)/N bytes per rank, the cost table of
+"Collectives from scratch").  Its whole output is compared, window by window,
+with the CPU checker (a literal NumPy simulation of the schedule,
+single-threaded) on the same inputs; the checker's time over all windows is
+the cpu_baseline, and the same windows spread over one host thread per
+affinity core give its all-cores time.  With --flush-mall a
 1 GiB buffer is overwritten before every timed call (outside the events) so
 that workloads smaller than the 256 MB Infinity Cache are read from HBM;
 value then comes from the event times.
@@ -158,25 +162,10 @@ def step_bytes(collective, n, t, isz, root=0):
     return (3 * reduced + 2 * (moved - reduced)) * isz
 
 
-def run_checker(collective, pristine, got, w, root, window, odt=None):
-    """Run the CPU checker over every window of the workload on the inputs in
-    `pristine`, compare with the device output `got`; returns (seconds,
-    compared elements, mismatching elements)."""
-    import numpy as np
+def _oracle_fn(collective, w, root, odt):
     import oracle
-    import torch
-
-    n, t = w.nranks, w.count
-    odt = odt or w.dtype          # the oracle's dtype name
-    owned = oracle.chunk_layout(n, t)
-
-    def host(x, a, b):
-        v = x[a:b]
-        if w.dtype == "bfloat16":
-            return v.view(torch.int16).cpu().numpy().view(np.uint16)
-        return v.cpu().numpy()
-
-    fn = {
+    t = w.count
+    return {
         "ring_allreduce": lambda x, a: oracle.ring_allreduce(x, "sum", odt, a, t),
         "tree_allreduce": lambda x, a: oracle.tree_allreduce(x, "sum", odt, 2, a, t),
         "reduce_scatter": lambda x, a: oracle.ring_reduce_scatter(x, "sum", odt, a, t),
@@ -187,17 +176,39 @@ def run_checker(collective, pristine, got, w, root, window, odt=None):
         "gather": lambda x, a: oracle.gather(x, root, odt, a, t),
         "alltoall": lambda x, a: oracle.alltoall(x, odt),
     }[collective]
+
+
+def host_copy(tensors, dtype):
+    """Whole device buffers as host NumPy arrays (bfloat16 as uint16 bits)."""
+    import numpy as np
+    import torch
+    if dtype == "bfloat16":
+        return [x.view(torch.int16).cpu().numpy().view(np.uint16) for x in tensors]
+    return [x.cpu().numpy() for x in tensors]
+
+
+def run_checker(collective, pristine, got, w, root, window, odt=None):
+    """Run the CPU checker over every window of the workload on the host
+    arrays `pristine` (the inputs), single-threaded, and compare with the
+    device output `got` (host arrays); returns (seconds in the checker,
+    compared elements, mismatching elements)."""
+    import numpy as np
+    import oracle
+
+    n, t = w.nranks, w.count
+    fn = _oracle_fn(collective, w, root, odt or w.dtype)
+    owned = oracle.chunk_layout(n, t)
     if collective == "alltoall":
         window = t   # an output element comes from another position: whole buffers
     secs, compared, bad = 0.0, 0, 0
     for a in range(0, t, window):
         b = min(t, a + window)
-        xin = [host(p, a, b) for p in pristine]
+        xin = [p[a:b] for p in pristine]
         t0 = time.perf_counter()
         want = fn(xin, a).bufs
         secs += time.perf_counter() - t0
         for r in range(n):
-            g = host(got[r], a, b)
+            g = got[r][a:b]
             if collective == "reduce_scatter":
                 lo, hi = max(owned[r][0], a) - a, min(owned[r][1], b) - a
                 if lo >= hi:
@@ -208,6 +219,39 @@ def run_checker(collective, pristine, got, w, root, window, odt=None):
             compared += g.size
             bad += int(np.count_nonzero(g != ww))
     return secs, compared, bad
+
+
+def time_checker_all_cores(collective, pristine, w, root, window, odt, workers):
+    """The same windowed CPU checker, its windows spread over `workers` host
+    threads (NumPy releases the GIL inside its array operations); returns the
+    wall time over all windows.  Results are not compared again: the
+    single-threaded pass already did that on the same inputs."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    t = w.count
+    fn = _oracle_fn(collective, w, root, odt or w.dtype)
+    if collective == "alltoall":
+        window = t
+    starts = list(range(0, t, window))
+
+    def one(a):
+        fn([p[a:min(t, a + window)] for p in pristine], a)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        list(pool.map(one, starts))
+    return time.perf_counter() - t0
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def run_one(args):
@@ -284,7 +328,7 @@ def run_one(args):
     wall = time.perf_counter() - t0
     gc.enable()
     event_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    finite = bool(all(torch.isfinite(b[:1 << 20].float()).all().item() for b in bufs[:2]))
+    finite = bool(all(torch.isfinite(b).all().item() for b in bufs))
     del flush_buf
 
     launch_ms = sum(event_ms) / len(event_ms)
@@ -365,12 +409,32 @@ def run_one(args):
               file=sys.stderr, flush=True)
         pristine = draw()
         got = [p.clone() for p in pristine]
+        ar.reset_counters()
         call(got)
         torch.cuda.synchronize()
-        secs, compared, bad = run_checker(ran, pristine, got, w, args.root, args.cpu_window, odt)
+        sent, recv, steps = ar.counters(n)
+        want_sent, want_recv = ar.expected_bytes(ran, n, t, odt, root=args.root)
+        result["counters"] = {
+            "sent": sent, "recv": recv, "steps": steps,
+            "closed_form_sent": want_sent, "closed_form_recv": want_recv,
+            "expected_steps": ar.expected_steps(ran, n),
+            "match": sent == want_sent and recv == want_recv and steps == ar.expected_steps(ran, n),
+        }
+        if ran == "ring_allreduce" and t % n == 0:
+            # the cost table's ring row: 2 T (N-1) / N bytes sent and received per rank
+            law = 2 * t * (n - 1) // n * isz
+            result["counters"]["ring_law_bytes_per_rank"] = law
+            result["counters"]["ring_law_holds"] = all(v == law for v in sent + recv)
+        host_in = host_copy(pristine, w.dtype)
+        host_out = host_copy(got, w.dtype)
         del pristine, got
         handles.clear()
         torch.cuda.empty_cache()
+        secs, compared, bad = run_checker(ran, host_in, host_out, w, args.root, args.cpu_window, odt)
+        del host_out
+        workers = len(os.sched_getaffinity(0))
+        secs_all = time_checker_all_cores(ran, host_in, w, args.root, args.cpu_window, odt, workers)
+        del host_in
         windows = -(-t // args.cpu_window)
         result["parity"] = {"compared_elements": compared, "mismatches": bad,
                             "bit_exact": bad == 0}
@@ -384,7 +448,17 @@ def run_one(args):
                       f"{args.cpu_window} elements per rank (literal NumPy simulation of "
                       f"the schedule, one thread), {secs:.2f} s",
             "seconds": round(secs, 3),
-            "host_cpus": len(os.sched_getaffinity(0)),
+            "all_cores": {
+                "value": round(t * isz / secs_all / 1e9, 4),
+                "unit": "GB/s",
+                "cores": workers,
+                "seconds": round(secs_all, 3),
+                "sample": f"the same {windows} windows spread over {workers} host threads "
+                          f"(one per affinity core), wall time",
+            },
+            "cpu_model": cpu_model(),
+            "os_cpu_count": os.cpu_count(),
+            "affinity_cores": workers,
         }
     return result
 
@@ -455,6 +529,7 @@ def main():
             sub = parse(base + ["--workload", wname, "--collective", coll, "--impl", impl] + extra)
             res = run_one(sub)
             failed |= not res.get("parity", {}).get("bit_exact", True)
+            failed |= not res.get("counters", {}).get("match", True)
             with open(args.suite, "a") as f:
                 f.write(json.dumps(res) + "\n")
             print(f"[suite] {wname} {coll} {impl} {' '.join(extra)}: "
@@ -469,8 +544,11 @@ def main():
     for path in filter(None, (args.jsonl, args.suite)):
         with open(path, "a") as f:
             f.write(line + "\n")
+    failed |= not result.get("counters", {}).get("match", True)
+    failed |= not result.get("counters", {}).get("ring_law_holds", True)
     if failed:
-        print("[bench] the device output differs from the CPU checker", file=sys.stderr)
+        print("[bench] the device output differs from the CPU checker, or the byte counters "
+              "differ from their closed forms", file=sys.stderr)
         sys.exit(1)
 
 

@@ -30,7 +30,7 @@
  * count   T, elements per rank.  Chunk layout: C = ceil(T/N), chunk c =
  *         [c*C, min(T, (c+1)*C)); only trailing chunks are short, and a chunk
  *         is empty when c*C >= T.  Rank c owns chunk c.
- * stream  a hipStream_t passed as void* (NULL = the null stream of the
+ * stream  a hipStream_t (NULL = the null stream of the
  *         calling thread's current device, which must then be the device
  *         that holds the buffers; a non-null stream carries its device).  Calls are
  *         asynchronous and stream-ordered: they enqueue kernels and return;
@@ -76,6 +76,11 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* The HIP stream handle, declared as HIP's runtime API declares it (an
+ * opaque pointer), so that this header needs no HIP include; including
+ * <hip/hip_runtime_api.h> before or after it is fine. */
+typedef struct ihipStream_t* hipStream_t;
 
 #ifdef __cplusplus
 extern "C" {
@@ -133,7 +138,7 @@ typedef enum { AR_IMPL_FUSED = 0, AR_IMPL_STEP = 1 } ar_impl_t;
  * i of chunk c, the fold x[c+1][i] (+) ... (+) x[c][i] taken in ring order
  * (each hop: the receiving rank's own value (+) the incoming partial). */
 ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                              ar_op_t op, void* stream);
+                              ar_op_t op, hipStream_t stream);
 
 /* Ring ReduceScatter [L09 3.6][SCR two-pass ring, first pass]: N-1 steps; at
  * step t rank r forwards chunk (r-t-1) mod N to rank r+1, which stores
@@ -142,7 +147,7 @@ ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dt
  * of every buffer are UNSPECIFIED afterwards (partials or inputs, depending
  * on the implementation). */
 ar_status_t ar_reduce_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                              ar_op_t op, void* stream);
+                              ar_op_t op, hipStream_t stream);
 
 /* Ring AllGather [L09 3.7][SCR two-pass ring, second pass]: the input of
  * rank r is chunk r of bufs[r] (its other chunks are ignored and
@@ -150,13 +155,13 @@ ar_status_t ar_reduce_scatter(void* const* bufs, int nranks, size_t count, ar_dt
  * rank r+1, which overwrites.  Afterwards every buffer holds every rank's
  * chunk. */
 ar_status_t ar_allgather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                         void* stream);
+                         hipStream_t stream);
 
 /* Broadcast [L09 3.1][SCR cost table: T bytes over a log2 N tree]: every
  * bufs[r] ends equal to bufs[root].  Schedule (and counters): a binomial tree
  * on roles (r - root) mod N, ceil(log2 N) rounds. */
 ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
-                         void* stream);
+                         hipStream_t stream);
 
 /* Double-binary-tree AllReduce [L09 5.2][CH4 4.3.2][SCR cost table:
  * 2 log2 N steps].  Two binomial trees reduce toward role 0 and broadcast
@@ -165,7 +170,7 @@ ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t
  * round k: role q (q mod 2^(k+1) == 0, q + 2^k < N) stores
  * own (+) value of role q + 2^k.  Every bufs[r] ends with role 0's result. */
 ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                              ar_op_t op, void* stream);
+                              ar_op_t op, hipStream_t stream);
 
 /* ---- rooted primitives ------------------------------------------------------ */
 
@@ -179,21 +184,21 @@ ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dt
  * buffer once to its parent; ceil(log2 N) steps.  root out of range ->
  * AR_ERROR_INVALID_ARGUMENT. */
 ar_status_t ar_reduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, ar_op_t op,
-                      int root, void* stream);
+                      int root, hipStream_t stream);
 
 /* Scatter from `root` [L09 3.2]: chunk c of bufs[root] (the ring chunk
  * layout above) is copied into chunk c of bufs[c] for every c != root; every
  * other element of every buffer is unchanged.  One step of N-1 direct
  * transfers. */
 ar_status_t ar_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
-                       void* stream);
+                       hipStream_t stream);
 
 /* Gather to `root` [L09 3.3]: chunk c of bufs[c] is copied into chunk c of
  * bufs[root] for every c != root, so the root holds every rank's shard in
  * rank order; the other buffers are unchanged.  One step of N-1 direct
  * transfers. */
 ar_status_t ar_gather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
-                      void* stream);
+                      hipStream_t stream);
 
 /* AllToAll [L09 3.8, lab 4 in 7.4]: every buffer is N equal blocks of
  * count/N elements; block j of bufs[i] is meant for rank j, which receives
@@ -203,7 +208,7 @@ ar_status_t ar_gather(void* const* bufs, int nranks, size_t count, ar_dtype_t dt
  * receives (N-1) blocks.  One kernel swaps block j of rank i with block i of
  * rank j for every pair i < j, under either implementation. */
 ar_status_t ar_alltoall(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                        void* stream);
+                        hipStream_t stream);
 
 /* ---- size-based choice between ring and tree ----------------------------- */
 
@@ -215,7 +220,7 @@ ar_status_t ar_alltoall(void* const* bufs, int nranks, size_t count, ar_dtype_t 
  * (the ring on a tie).  Arguments, errors and counters are those of the call
  * it runs; its result is that call's result bit for bit. */
 ar_status_t ar_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                         ar_op_t op, void* stream);
+                         ar_op_t op, hipStream_t stream);
 
 /* The collective ar_allreduce would run (AR_RING_ALLREDUCE or
  * AR_TREE_ALLREDUCE) for these arguments under the current implementation.
@@ -262,10 +267,13 @@ ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar
  * N == 1); -1 on a bad argument. */
 int ar_expected_steps(ar_collective_t coll, int nranks);
 
-/* Process-wide cumulative counters since load or the last reset.  Copies the
- * first nranks entries (nranks <= AR_MAX_RANKS) into sent / recv, and the
- * total schedule steps into *steps (any output may be NULL).  Thread-safe. */
-ar_status_t ar_counters_read(int nranks, uint64_t* sent, uint64_t* recv, uint64_t* steps);
+/* Process-wide cumulative counters since load or the last reset [SCR
+ * exercises: per-rank byte counter].  Copies the first nranks entries
+ * (0 <= nranks <= AR_MAX_RANKS) of the logical bytes each rank sent and
+ * received into sent / recv (either may be NULL).  Thread-safe. */
+ar_status_t ar_counters_read(int nranks, uint64_t* sent, uint64_t* recv);
+/* Total schedule steps counted since load or the last reset. */
+uint64_t ar_counters_steps(void);
 void ar_counters_reset(void);
 
 /* Process-wide choice of implementation for subsequent calls (initially

@@ -195,7 +195,7 @@ def test_host_helpers_reject_bad_arguments():
     assert lib.ar_expected_bytes(9, 4, 10, 1, 0, buf, buf) == 1
     assert lib.ar_expected_bytes(3, 4, 10, 1, 4, buf, buf) == 1
     assert lib.ar_expected_steps(0, 0) == -1 and lib.ar_expected_steps(0, 65) == -1
-    assert lib.ar_counters_read(65, None, None, None) == 1
+    assert lib.ar_counters_read(65, None, None) == 1
     assert lib.ar_chunk_size(0, 10) == 0
 
 

@@ -152,3 +152,19 @@ def test_suite_rows_are_valid():
         assert impl in ("fused", "step")
         args = bench.parse(["--workload", wname, "--collective", coll, "--impl", impl] + extra)
         assert args.warmup + args.steps <= bench.MAX_CALLS
+
+
+@pytest.mark.parametrize("coll", ["ring_allreduce", "reduce_scatter", "tree_allreduce", "alltoall"])
+def test_checker_finds_planted_mismatch_and_all_cores_pass_runs(coll):
+    """The bench's windowed checker (host arrays in, host arrays out) reports no
+    mismatch on the oracle's own output, exactly one after one output element
+    is changed, and its all-cores timing pass runs over the same windows."""
+    w = workloads.Workload("tiny", 4, 1000, "float32", "normal", 9, {"std": 1.0})
+    x = workloads.host_inputs(w.nranks, w.count, w.dtype, w.dist, w.seed, w.params)
+    fn = bench._oracle_fn(coll, w, 0, w.dtype)
+    got = [b.copy() for b in fn(x, 0).bufs]
+    secs, compared, bad = bench.run_checker(coll, x, got, w, 0, 256)
+    assert bad == 0 and compared > 0 and secs >= 0
+    got[1][0 if coll != "reduce_scatter" else 250] += 1.0
+    assert bench.run_checker(coll, x, got, w, 0, 256)[2] == 1
+    assert bench.time_checker_all_cores(coll, x, w, 0, 256, w.dtype, 3) >= 0

@@ -44,7 +44,8 @@ SIGNATURES = {
     "ar_chunk_range": (_I, [_I, _SZ, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "ar_expected_bytes": (_I, [_I, _I, _SZ, _I, _I, _U64P, _U64P]),
     "ar_expected_steps": (_I, [_I, _I]),
-    "ar_counters_read": (_I, [_I, _U64P, _U64P, _U64P]),
+    "ar_counters_read": (_I, [_I, _U64P, _U64P]),
+    "ar_counters_steps": (ctypes.c_uint64, []),
     "ar_counters_reset": (None, []),
     "ar_set_impl": (_I, [_I]),
     "ar_get_impl": (_I, []),
@@ -390,9 +391,8 @@ def expected_steps(collective, nranks):
 def counters(nranks):
     sent = (ctypes.c_uint64 * max(1, nranks))()
     recv = (ctypes.c_uint64 * max(1, nranks))()
-    steps = ctypes.c_uint64()
-    _check(lib().ar_counters_read(nranks, sent, recv, ctypes.byref(steps)), "counters")
-    return list(sent)[:nranks], list(recv)[:nranks], steps.value
+    _check(lib().ar_counters_read(nranks, sent, recv), "counters")
+    return list(sent)[:nranks], list(recv)[:nranks], lib().ar_counters_steps()
 
 
 def reset_counters():

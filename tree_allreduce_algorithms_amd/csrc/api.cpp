@@ -93,7 +93,7 @@ void add_counters(ar_collective_t coll, int n, uint64_t count, int root, size_t 
 }
 
 ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar_dtype_t dtype,
-                int op, int root, void* stream_ptr) {
+                int op, int root, hipStream_t stream) {
   // dtype may be rewritten below (bfloat16 copies); counters use its size,
   // which the rewrite keeps
   const ar_status_t v = ar::validate(bufs, n, count, static_cast<int>(dtype), op, root);
@@ -111,7 +111,6 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
     ptrs.p[r] = bufs[r];
     aligned16 = aligned16 && (reinterpret_cast<uintptr_t>(bufs[r]) % 16 == 0);
   }
-  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   // bfloat16 with float32 partials: the reductions can only run fused (a
   // partial cannot live in a bfloat16 buffer between launches); the copies
   // are bfloat16 copies.
@@ -175,61 +174,61 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
 extern "C" {
 
 ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                              ar_op_t op, void* stream) {
+                              ar_op_t op, hipStream_t stream) {
   if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_RING_ALLREDUCE, bufs, nranks, count, dtype, static_cast<int>(op), -1, stream);
 }
 
 ar_status_t ar_reduce_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                              ar_op_t op, void* stream) {
+                              ar_op_t op, hipStream_t stream) {
   if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_REDUCE_SCATTER, bufs, nranks, count, dtype, static_cast<int>(op), -1, stream);
 }
 
 ar_status_t ar_allgather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                         void* stream) {
+                         hipStream_t stream) {
   return run(AR_ALLGATHER, bufs, nranks, count, dtype, -1, -1, stream);
 }
 
 ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
-                         void* stream) {
+                         hipStream_t stream) {
   if (root < 0) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_BROADCAST, bufs, nranks, count, dtype, -1, root, stream);
 }
 
 ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                              ar_op_t op, void* stream) {
+                              ar_op_t op, hipStream_t stream) {
   if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_TREE_ALLREDUCE, bufs, nranks, count, dtype, static_cast<int>(op), -1, stream);
 }
 
 ar_status_t ar_reduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, ar_op_t op,
-                      int root, void* stream) {
+                      int root, hipStream_t stream) {
   if (!ar::op_ok(static_cast<int>(op)) || root < 0) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_REDUCE, bufs, nranks, count, dtype, static_cast<int>(op), root, stream);
 }
 
 ar_status_t ar_scatter(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
-                       void* stream) {
+                       hipStream_t stream) {
   if (root < 0) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_SCATTER, bufs, nranks, count, dtype, -1, root, stream);
 }
 
 ar_status_t ar_gather(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, int root,
-                      void* stream) {
+                      hipStream_t stream) {
   if (root < 0) return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_GATHER, bufs, nranks, count, dtype, -1, root, stream);
 }
 
 ar_status_t ar_alltoall(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
-                        void* stream) {
+                        hipStream_t stream) {
   if (nranks >= 1 && nranks <= AR_MAX_RANKS && count % static_cast<size_t>(nranks) != 0)
     return AR_ERROR_INVALID_ARGUMENT;
   return run(AR_ALLTOALL, bufs, nranks, count, dtype, -1, -1, stream);
 }
 
 ar_status_t ar_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype, ar_op_t op,
-                         void* stream) {
+                         hipStream_t stream) {
   if (!ar::op_ok(static_cast<int>(op))) return AR_ERROR_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > AR_MAX_RANKS || !ar::dtype_ok(static_cast<int>(dtype)))
     return AR_ERROR_INVALID_ARGUMENT;
@@ -301,15 +300,19 @@ ar_status_t ar_expected_bytes(ar_collective_t coll, int nranks, size_t count, ar
 
 int ar_expected_steps(ar_collective_t coll, int nranks) { return ar::expected_steps(coll, nranks); }
 
-ar_status_t ar_counters_read(int nranks, uint64_t* sent, uint64_t* recv, uint64_t* steps) {
+ar_status_t ar_counters_read(int nranks, uint64_t* sent, uint64_t* recv) {
   if (nranks < 0 || nranks > AR_MAX_RANKS) return AR_ERROR_INVALID_ARGUMENT;
   std::lock_guard<std::mutex> lock(g_counter_mu);
   for (int r = 0; r < nranks; ++r) {
     if (sent != nullptr) sent[r] = g_sent[r];
     if (recv != nullptr) recv[r] = g_recv[r];
   }
-  if (steps != nullptr) *steps = g_steps;
   return AR_SUCCESS;
+}
+
+uint64_t ar_counters_steps(void) {
+  std::lock_guard<std::mutex> lock(g_counter_mu);
+  return g_steps;
 }
 
 void ar_counters_reset(void) {
