@@ -59,8 +59,9 @@
  *           AR_ERROR_UNSUPPORTED       a valid request this build lacks;
  *           AR_ERROR_HIP               a kernel launch failed; the hipError_t
  *               is kept for ar_last_hip_error().  With the step
- *               implementation the launches of earlier steps may already be
- *               enqueued, so the buffers are then unspecified.  (Faults
+ *               implementation (or a fused ring AllReduce that runs as two
+ *               launches) the launches before the failing one may already
+ *               be enqueued, so the buffers are then unspecified.  (Faults
  *               during execution surface at the caller's next
  *               synchronisation.)
  *         count == 0 or nranks == 1 is a valid no-op (AR_SUCCESS, nothing
@@ -136,7 +137,10 @@ typedef enum { AR_IMPL_FUSED = 0, AR_IMPL_STEP = 1 } ar_impl_t;
 /* Ring AllReduce [L09 3.5, 3.9, 4.3][CH4 4.3.1][SCR two-pass ring]:
  * ReduceScatter then AllGather.  Afterwards every bufs[r] holds, at element
  * i of chunk c, the fold x[c+1][i] (+) ... (+) x[c][i] taken in ring order
- * (each hop: the receiving rank's own value (+) the incoming partial). */
+ * (each hop: the receiving rank's own value (+) the incoming partial).
+ * AR_IMPL_FUSED: one fold storing into every rank; from 32 ranks and 256 MiB
+ * of inputs (nranks * count * element size) up, the fused ReduceScatter and
+ * then the fused AllGather (two launches, the same bits, faster there). */
 ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
                               ar_op_t op, hipStream_t stream);
 

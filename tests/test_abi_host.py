@@ -214,6 +214,8 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
     if coll == "alltoall":               # every off-diagonal block read and written once
         return 2 * n * (n - 1) * (t // n) * s
     if impl == "fused" and coll not in ("scatter", "gather"):
+        if coll == "ring_allreduce" and _split(n, t, s):
+            return (2 * n + 1) * t * s     # ReduceScatter (N+1) T s, then AllGather N T s
         return {"ring_allreduce": 2 * n * t, "tree_allreduce": 2 * n * t,
                 "reduce_scatter": (n + 1) * t, "allgather": n * t, "broadcast": n * t}[coll] * s
     x = [np.zeros(t, np.int32) for _ in range(n)]
@@ -223,6 +225,12 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
     return (3 * reduced + 2 * (moved - reduced)) * s
 
 
+def _split(n, t, s):
+    """The fused ring AllReduce runs as ReduceScatter then AllGather from 32
+    ranks and 256 MiB of inputs up (the documented rule of ar.h)."""
+    return n >= 32 and n * t * s >= 1 << 28
+
+
 @pytest.mark.parametrize("coll", sorted(ORACLE_CALLS))
 @pytest.mark.parametrize("impl", ["fused", "step"])
 @pytest.mark.parametrize("n,t,dtype", [(4, 256, "float32"), (8, 100_003, "bfloat16"),
@@ -230,10 +238,27 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
 def test_predicted_time_is_the_documented_formula(coll, impl, n, t, dtype):
     alpha, gbps = ar.get_cost_model(coll, impl)
     launches = 1 if impl == "fused" or coll in ("reduce", "alltoall") else ar.expected_steps(coll, n)
+    if impl == "fused" and coll == "ring_allreduce" and _split(n, t, 2 if dtype == "bfloat16" else 4):
+        launches = 2
     if n == 1:
         launches = 0
     want = launches * alpha + _oracle_hbm_bytes(coll, impl, n, t, dtype) / (gbps * 1e3)
     assert ar.predict_time(coll, impl, n, t, dtype) == pytest.approx(want, rel=1e-12)
+
+
+@pytest.mark.parametrize("n,t,dtype", [(64, 1_048_576, "float32"), (32, 4_194_304, "bfloat16"),
+                                       (32, 2_097_151, "float32"), (31, 100_000_000, "float32"),
+                                       (64, 1_048_575, "float32"), (64, 16_777_217, "float32")])
+def test_fused_ring_allreduce_split_is_modelled(n, t, dtype):
+    """From 32 ranks and 256 MiB of inputs the fused ring AllReduce is two
+    launches moving (2N+1) T s bytes; below either bound one launch of 2N T s."""
+    s = 2 if dtype == "bfloat16" else 4
+    alpha, gbps = ar.get_cost_model("ring_allreduce", "fused")
+    split = _split(n, t, s)
+    assert split == (n >= 32 and n * t * s >= 1 << 28)
+    launches, nbytes = (2, (2 * n + 1) * t * s) if split else (1, 2 * n * t * s)
+    want = launches * alpha + nbytes / (gbps * 1e3)
+    assert ar.predict_time("ring_allreduce", "fused", n, t, dtype) == pytest.approx(want, rel=1e-12)
 
 
 def test_allreduce_choice_switches_at_the_model_crossover():

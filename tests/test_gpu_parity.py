@@ -506,6 +506,76 @@ def test_zero_n64_reduce_scatter_then_allgather_and_broadcast():
     ar.set_impl("fused")
 
 
+def test_split_ring_allreduce_many_ranks():
+    """From 32 ranks and 256 MiB of inputs the fused ring AllReduce runs as the
+    fused ReduceScatter followed by the fan-out AllGather.  N=64 x 16,777,217
+    float32 (ragged chunks): sampled windows against the oracle and whole
+    buffers against the step implementation (the literal schedule); N=32 x
+    16,777,259 bfloat16, per hop and with float32 partials: sampled windows."""
+    w = workloads.WORKLOADS["zero_n64"]
+    size = -(-w.count // w.nranks)
+    cuts = [c * size for c in range(1, w.nranks, 9)] + [63 * size]
+    ar.set_impl("fused")
+    a = _device_inputs(w)
+    check_windows("ring_allreduce", a, lambda b: ar.ring_allreduce(b), w.dtype, cuts=cuts,
+                  seed=9, ranks=[0, 17, 63])
+    assert _ranks_identical(a)
+    ar.set_impl("step")
+    b = _device_inputs(w)
+    announce("ring_allreduce impl=step n=64 whole buffers")
+    ar.ring_allreduce(b)
+    torch.cuda.synchronize()
+    ar.set_impl("fused")
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    n, t = 32, 16_777_259
+    size = -(-t // n)
+    wins = _windows(t, [c * size for c in range(1, n, 5)], 21)
+    for acc in (None, "float32"):
+        bufs = [workloads.device_rank("normal", "bfloat16", t, 21, r, DEV, {"std": 1e-3})
+                for r in range(n)]
+        saved = [(lo, hi, _window_host(bufs, lo, hi, "bfloat16")) for lo, hi in wins]
+        announce(f"ring_allreduce n={n} t={t} bfloat16 accumulate={acc}")
+        ar.ring_allreduce(bufs, accumulate=acc)
+        torch.cuda.synchronize()
+        odt = "bfloat16_acc32" if acc else "bfloat16"
+        for lo, hi, xin in saved:
+            want = oracle.ring_allreduce(xin, "sum", odt, window_start=lo, total=t).bufs
+            for r in (0, 13, 31):
+                assert_same(to_host(bufs[r][lo:hi], "bfloat16"), want[r], "bfloat16",
+                            f"{odt} window {lo} rank {r}")
+        assert _ranks_identical(bufs)
+        del bufs, saved
+        torch.cuda.empty_cache()
+    # int32 MAX at the smallest split size class: fused (two launches) on
+    # sampled windows against the oracle, and whole buffers against the
+    # literal schedule
+    n, t = 32, 2_097_157
+    size = -(-t // n)
+
+    def draw():
+        return [workloads.device_rank("int_uniform", "int32", t, 23, r, DEV, {"lo": -100, "hi": 100})
+                for r in range(n)]
+
+    outs = []
+    for impl in ("fused", "step"):
+        ar.set_impl(impl)
+        bufs = draw()
+        if impl == "fused":
+            check_windows("ring_allreduce", bufs, lambda b: ar.ring_allreduce(b, op="max"), "int32",
+                          op="max", cuts=[c * size for c in range(1, n, 7)], seed=23, ranks=[0, 31])
+        else:
+            announce(f"ring_allreduce max n={n} t={t} int32 impl=step")
+            ar.ring_allreduce(bufs, op="max")
+            torch.cuda.synchronize()
+        outs.append(bufs)
+    ar.set_impl("fused")
+    assert all(torch.equal(x, y) for x, y in zip(*outs))
+    del outs
+    torch.cuda.empty_cache()
+
+
 def test_zero_n64_reduce_scatter_gather_full_size():
     """N=64, T=16,777,217 float32 (ragged chunks): Reduce, Scatter and Gather
     to a root in the middle, on sampled windows; the ranks that the pages say

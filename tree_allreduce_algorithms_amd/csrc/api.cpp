@@ -68,7 +68,7 @@ double predict_us(ar_collective_t coll, ar_impl_t impl, int n, size_t count, ar_
     std::lock_guard<std::mutex> lock(g_cost_mu);
     c = g_cost[coll][impl];
   }
-  const double launches = ar::impl_launches(coll, impl, n);
+  const double launches = ar::impl_launches(coll, impl, n, count, ar::itemsize(dtype));
   const double bytes = static_cast<double>(ar::impl_hbm_bytes(coll, impl, n, count, ar::itemsize(dtype)));
   return launches * c.alpha_us + bytes / (c.gbps * 1e3);
 }
@@ -143,7 +143,15 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
   } else {
     switch (coll) {
       case AR_RING_ALLREDUCE:
-        err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, true, vec, stream);
+        if (ar::ring_allreduce_split(n, count, ar::itemsize(dtype))) {
+          // fused ReduceScatter, then the owners' chunks fanned out: the same
+          // bits as the one-pass fold (AllReduce = AllGather after
+          // ReduceScatter), faster for many ranks
+          err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, vec, stream);
+          if (err == hipSuccess) err = ar::launch_fanout(ptrs, n, count, dtype, false, 0, vec, stream);
+        } else {
+          err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, true, vec, stream);
+        }
         break;
       case AR_REDUCE_SCATTER:
         err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, vec, stream);

@@ -291,10 +291,19 @@ int expected_steps(ar_collective_t coll, int n) {
   return -1;
 }
 
-int impl_launches(ar_collective_t coll, ar_impl_t impl, int n) {
+bool ring_allreduce_split(int n, uint64_t count, size_t isz) {
+  constexpr int kMinRanks = 32;
+  constexpr uint64_t kMinInputBytes = 1ull << 28;
+  return n >= kMinRanks && static_cast<uint64_t>(n) * count * isz >= kMinInputBytes;
+}
+
+int impl_launches(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz) {
+  if (n <= 1) return 0;
+  if (impl == AR_IMPL_FUSED && coll == AR_RING_ALLREDUCE && ring_allreduce_split(n, count, isz))
+    return 2;
   // Reduce has one (fused) implementation; Scatter, Gather and AllToAll are
   // one step.
-  if (impl == AR_IMPL_FUSED || coll == AR_REDUCE || coll == AR_ALLTOALL) return n > 1 ? 1 : 0;
+  if (impl == AR_IMPL_FUSED || coll == AR_REDUCE || coll == AR_ALLTOALL) return 1;
   return expected_steps(coll, n);
 }
 
@@ -308,6 +317,7 @@ uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t co
   if (fused && coll != AR_SCATTER && coll != AR_GATHER && coll != AR_ALLTOALL) {
     switch (coll) {
       case AR_RING_ALLREDUCE:
+        return (ring_allreduce_split(n, count, isz) ? 2 * un + 1 : 2 * un) * count * isz;
       case AR_TREE_ALLREDUCE: return 2 * un * count * isz;
       case AR_REDUCE_SCATTER:
       case AR_REDUCE: return (un + 1) * count * isz;

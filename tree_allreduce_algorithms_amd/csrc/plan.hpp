@@ -69,8 +69,24 @@ int expected_steps(ar_collective_t coll, int n);
 // launches once per schedule step and moves 3 bytes per element of each
 // reduce transfer (read both sides, write one) and 2 per element of each copy
 // transfer.
-int impl_launches(ar_collective_t coll, ar_impl_t impl, int n);
+// The fused ring AllReduce of many ranks runs as two launches (see
+// ring_allreduce_split), moving (2N + 1) * T * s bytes.
+int impl_launches(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz);
 uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz);
+
+// Whether the fused ring AllReduce runs as the fused ReduceScatter (every
+// element folded in ring order into its owner's chunk) followed by the fused
+// AllGather (each owner's chunk copied to every other rank) instead of one
+// fold that stores into all N ranks.  Both give the same bits: AllReduce is
+// AllGather after ReduceScatter [Lecture 09 section 3.9], and the
+// ReduceScatter leaves exactly the value the one-pass fold stores.  Measured
+// on gfx950 (in-process A/B, float32), the two phases win from 32 ranks up
+// although they move T * s more bytes: one phase mostly reads and the other
+// mostly writes, while the one-pass fold mixes a read and a write stream per
+// rank.  With 9.6 GB of inputs: N = 16 -2 %, 24 +1 %, 32 +2-3 %, 48 +6.5 %,
+// 64 +8 %; with 256 MiB of inputs: N = 32 +6 %, N = 64 +17 %.  With 64 MiB
+// (N = 64, Infinity-Cache resident) the one-pass fold is 13 % faster.
+bool ring_allreduce_split(int n, uint64_t count, size_t isz);
 
 // Validation shared by every collective call.  `op` < 0 means "not used",
 // `root` < 0 means "not used".  Checks: bufs non-NULL, n in range, dtype /
