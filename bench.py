@@ -61,17 +61,21 @@ DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
 MAX_CALLS = 35
 COLLECTIVES = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce",
                "allreduce", "reduce", "scatter", "gather", "alltoall"]
-KERNEL = {  # collective, impl -> kernel that dominates one call
-    ("ring_allreduce", "fused"): "ring_fold_kernel",
-    ("reduce_scatter", "fused"): "ring_fold_kernel",
-    ("allgather", "fused"): "fanout_kernel",
-    ("broadcast", "fused"): "fanout_kernel",
-    ("tree_allreduce", "fused"): "tree_fold_kernel",
-    ("reduce", "fused"): "tree_fold_kernel",
-    ("reduce", "step"): "tree_fold_kernel",   # Reduce has one (fused) implementation
-    ("alltoall", "fused"): "alltoall_kernel",
-    ("alltoall", "step"): "alltoall_kernel",
-}
+STAGE_MAX_RANKS = 32   # the folds run through LDS-staged tiles for 2 to 32 ranks
+
+
+def kernel_name(collective, impl, n):
+    """The kernel that dominates one call (16-byte aligned rank buffers)."""
+    staged = 2 <= n <= STAGE_MAX_RANKS
+    if collective in ("ring_allreduce", "reduce_scatter") and impl == "fused":
+        return "ring_stage_kernel" if staged else "ring_fold_kernel"
+    if collective == "tree_allreduce" and impl == "fused" or collective == "reduce":
+        return "tree_stage_kernel" if staged else "tree_fold_kernel"
+    if collective in ("allgather", "broadcast") and impl == "fused":
+        return "fanout_kernel"
+    if collective == "alltoall":
+        return "alltoall_kernel"
+    return "step_kernel"
 
 
 def parse(argv=None):
@@ -100,18 +104,29 @@ def parse(argv=None):
     return p.parse_args(argv)
 
 
-def kernel_source_hash():
-    """sha256 over every device-code source of the library (sorted by name)."""
+KERNEL_FILE = {  # kernel -> the source file that defines it
+    "ring_stage_kernel": "ring_kernels.hip", "ring_fold_kernel": "ring_kernels.hip",
+    "tree_stage_kernel": "tree_kernels.hip", "tree_fold_kernel": "tree_kernels.hip",
+    "fanout_kernel": "copy_kernels.hip", "alltoall_kernel": "copy_kernels.hip",
+    "step_kernel": "step_kernels.hip",
+}
+
+
+def kernel_source_hash(kernel=None):
+    """sha256 over the device code a kernel is built from: its own source file
+    plus every shared header (all device sources when kernel is None), in
+    name order."""
     csrc = os.path.join(ROOT, "tree_allreduce_algorithms_amd", "csrc")
+    own = KERNEL_FILE.get(kernel)
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
+        if name.endswith(".hpp") or (name.endswith(".hip") and (own is None or name == own)):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def traffic_from_profile(workload, collective, impl, per_call=False, accumulate=None):
+def traffic_from_profile(workload, collective, impl, per_call=False, accumulate=None, kernel=None):
     """HBM bytes per launch (per call for a multi-launch implementation, with
     per_call) from the committed PMC summary of this implementation and
     workload (and accumulator: bfloat16 with float32 partials is a kernel of
@@ -124,7 +139,7 @@ def traffic_from_profile(workload, collective, impl, per_call=False, accumulate=
     key = "hbm_bytes_per_call" if per_call else "hbm_bytes_per_launch"
     sha = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
     val = re.search(rf"^{key}:\s*([0-9]+)\s*$", text, re.M)
-    if not sha or not val or sha.group(1) != kernel_source_hash():
+    if not sha or not val or sha.group(1) != kernel_source_hash(kernel):
         return None
     return int(val.group(1))
 
@@ -341,8 +356,9 @@ def run_one(args):
     launches = 1 if fused else ar.expected_steps(ran, n)
     moved = alg if fused else step_bytes(ran, n, t, isz, args.root)
     achieved = moved / (launch_ms * 1e-3) / 1e9
+    kernel = kernel_name(ran, args.impl, n)
     traffic = traffic_from_profile(w.name, args.collective, args.impl, per_call=launches > 1,
-                                   accumulate=acc)
+                                   accumulate=acc, kernel=None if launches > 1 else kernel)
 
     result = {
         "metric": METRIC,
@@ -371,7 +387,7 @@ def run_one(args):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": KERNEL.get((ran, args.impl), "step_kernel"),
+            "kernel": kernel,
             "algorithmic_bytes_per_launch": moved if launches == 1 else None,
             "algorithmic_bytes_per_call": moved,
             "launches_per_step": launches,

@@ -138,7 +138,7 @@ typedef enum { AR_IMPL_FUSED = 0, AR_IMPL_STEP = 1 } ar_impl_t;
  * ReduceScatter then AllGather.  Afterwards every bufs[r] holds, at element
  * i of chunk c, the fold x[c+1][i] (+) ... (+) x[c][i] taken in ring order
  * (each hop: the receiving rank's own value (+) the incoming partial).
- * AR_IMPL_FUSED: one fold storing into every rank; from 32 ranks and 256 MiB
+ * AR_IMPL_FUSED: one fold storing into every rank; from 33 ranks and 256 MiB
  * of inputs (nranks * count * element size) up, the fused ReduceScatter and
  * then the fused AllGather (two launches, the same bits, faster there). */
 ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,

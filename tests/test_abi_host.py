@@ -226,9 +226,9 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
 
 
 def _split(n, t, s):
-    """The fused ring AllReduce runs as ReduceScatter then AllGather from 32
+    """The fused ring AllReduce runs as ReduceScatter then AllGather from 33
     ranks and 256 MiB of inputs up (the documented rule of ar.h)."""
-    return n >= 32 and n * t * s >= 1 << 28
+    return n >= 33 and n * t * s >= 1 << 28
 
 
 @pytest.mark.parametrize("coll", sorted(ORACLE_CALLS))
@@ -246,16 +246,17 @@ def test_predicted_time_is_the_documented_formula(coll, impl, n, t, dtype):
     assert ar.predict_time(coll, impl, n, t, dtype) == pytest.approx(want, rel=1e-12)
 
 
-@pytest.mark.parametrize("n,t,dtype", [(64, 1_048_576, "float32"), (32, 4_194_304, "bfloat16"),
-                                       (32, 2_097_151, "float32"), (31, 100_000_000, "float32"),
+@pytest.mark.parametrize("n,t,dtype", [(64, 1_048_576, "float32"), (33, 4_194_304, "bfloat16"),
+                                       (32, 100_000_000, "float32"), (33, 2_033_601, "float32"),
+                                       (33, 2_033_600, "float32"), (31, 100_000_000, "float32"),
                                        (64, 1_048_575, "float32"), (64, 16_777_217, "float32")])
 def test_fused_ring_allreduce_split_is_modelled(n, t, dtype):
-    """From 32 ranks and 256 MiB of inputs the fused ring AllReduce is two
+    """From 33 ranks and 256 MiB of inputs the fused ring AllReduce is two
     launches moving (2N+1) T s bytes; below either bound one launch of 2N T s."""
     s = 2 if dtype == "bfloat16" else 4
     alpha, gbps = ar.get_cost_model("ring_allreduce", "fused")
     split = _split(n, t, s)
-    assert split == (n >= 32 and n * t * s >= 1 << 28)
+    assert split == (n >= 33 and n * t * s >= 1 << 28)
     launches, nbytes = (2, (2 * n + 1) * t * s) if split else (1, 2 * n * t * s)
     want = launches * alpha + nbytes / (gbps * 1e3)
     assert ar.predict_time("ring_allreduce", "fused", n, t, dtype) == pytest.approx(want, rel=1e-12)

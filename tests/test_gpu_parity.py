@@ -507,10 +507,10 @@ def test_zero_n64_reduce_scatter_then_allgather_and_broadcast():
 
 
 def test_split_ring_allreduce_many_ranks():
-    """From 32 ranks and 256 MiB of inputs the fused ring AllReduce runs as the
+    """From 33 ranks and 256 MiB of inputs the fused ring AllReduce runs as the
     fused ReduceScatter followed by the fan-out AllGather.  N=64 x 16,777,217
     float32 (ragged chunks): sampled windows against the oracle and whole
-    buffers against the step implementation (the literal schedule); N=32 x
+    buffers against the step implementation (the literal schedule); N=40 x
     16,777,259 bfloat16, per hop and with float32 partials: sampled windows."""
     w = workloads.WORKLOADS["zero_n64"]
     size = -(-w.count // w.nranks)
@@ -529,7 +529,7 @@ def test_split_ring_allreduce_many_ranks():
     assert all(torch.equal(x, y) for x, y in zip(a, b))
     del a, b
     torch.cuda.empty_cache()
-    n, t = 32, 16_777_259
+    n, t = 40, 16_777_259
     size = -(-t // n)
     wins = _windows(t, [c * size for c in range(1, n, 5)], 21)
     for acc in (None, "float32"):
@@ -542,7 +542,7 @@ def test_split_ring_allreduce_many_ranks():
         odt = "bfloat16_acc32" if acc else "bfloat16"
         for lo, hi, xin in saved:
             want = oracle.ring_allreduce(xin, "sum", odt, window_start=lo, total=t).bufs
-            for r in (0, 13, 31):
+            for r in (0, 13, 39):
                 assert_same(to_host(bufs[r][lo:hi], "bfloat16"), want[r], "bfloat16",
                             f"{odt} window {lo} rank {r}")
         assert _ranks_identical(bufs)
@@ -551,7 +551,7 @@ def test_split_ring_allreduce_many_ranks():
     # int32 MAX at the smallest split size class: fused (two launches) on
     # sampled windows against the oracle, and whole buffers against the
     # literal schedule
-    n, t = 32, 2_097_157
+    n, t = 33, 2_033_603
     size = -(-t // n)
 
     def draw():
@@ -564,7 +564,7 @@ def test_split_ring_allreduce_many_ranks():
         bufs = draw()
         if impl == "fused":
             check_windows("ring_allreduce", bufs, lambda b: ar.ring_allreduce(b, op="max"), "int32",
-                          op="max", cuts=[c * size for c in range(1, n, 7)], seed=23, ranks=[0, 31])
+                          op="max", cuts=[c * size for c in range(1, n, 7)], seed=23, ranks=[0, 32])
         else:
             announce(f"ring_allreduce max n={n} t={t} int32 impl=step")
             ar.ring_allreduce(bufs, op="max")
@@ -764,6 +764,49 @@ def test_acc32_parity(coll, shape):
                 else:
                     assert_same(got, want[r], "bfloat16", f"{coll}/{op}/{impl} rank {r}")
     ar.set_impl("fused")
+
+
+def _stage_tile_elems(n, itemsize):
+    """Elements per rank in one tile of the LDS-staged folds: M runs of 64
+    16-byte packs, M = 4 for N <= 2, 2 for N <= 4, else 1."""
+    runs = 4 if n <= 2 else 2 if n <= 4 else 1
+    return runs * 64 * (16 // itemsize)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 6, 8, 9, 16, 17, 31, 32, 33])
+def test_staged_tile_boundaries(n):
+    """The staged folds at every rank-count bucket (2, 4, 8, 16, 32 ranks and
+    one past each): chunks of about 3.5 tiles, so that first and last tiles
+    are partial and chunk starts fall inside tiles, plus a tiny T whose
+    chunks hold no whole 16-byte pack.  Ring AllReduce and ReduceScatter,
+    double tree and Reduce, every dtype including float32 partials, against
+    the oracle bit for bit."""
+    for dtype in ("float32", "bfloat16", "int32", "acc32"):
+        isz = 2 if dtype in ("bfloat16", "acc32") else 4
+        for t in (n * (7 * _stage_tile_elems(n, isz) // 2) + 7, 3 * n + 1):
+            host_dt = "bfloat16" if dtype == "acc32" else dtype
+            dist = "int_uniform" if dtype == "int32" else "normal"
+            x = workloads.host_inputs(n, t, host_dt, dist, 400 + n + t % 97, _params(dist, n))
+            root = (2 * n) // 3
+            owned = oracle.chunk_layout(n, t)
+            for coll in ("ring_allreduce", "reduce_scatter", "tree_allreduce", "reduce"):
+                for op in (("sum", "max") if dtype == "float32" else ("sum",)):
+                    announce(f"staged {coll} n={n} t={t} dtype={dtype} op={op}")
+                    if dtype == "acc32":
+                        run, want = ACC32_CALLS[coll][0], ACC32_CALLS[coll][1](x, op, root).bufs
+                    else:
+                        run, want = CALLS[coll][0], CALLS[coll][1](x, op, host_dt, root).bufs
+                    bufs = to_dev(x, host_dt)
+                    run(bufs, op, root)
+                    torch.cuda.synchronize()
+                    for r in range(n):
+                        got = to_host(bufs[r], host_dt)
+                        if coll == "reduce_scatter":
+                            lo, hi = owned[r]
+                            got, w_ = got[lo:hi], want[r][lo:hi]
+                        else:
+                            w_ = want[r]
+                        assert_same(got, w_, host_dt, f"staged {coll} {dtype} {op} rank {r}")
 
 
 def test_acc32_large_gradient_windows():

@@ -292,7 +292,7 @@ int expected_steps(ar_collective_t coll, int n) {
 }
 
 bool ring_allreduce_split(int n, uint64_t count, size_t isz) {
-  constexpr int kMinRanks = 32;
+  constexpr int kMinRanks = 33;
   constexpr uint64_t kMinInputBytes = 1ull << 28;
   return n >= kMinRanks && static_cast<uint64_t>(n) * count * isz >= kMinInputBytes;
 }

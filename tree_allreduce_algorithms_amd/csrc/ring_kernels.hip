@@ -102,6 +102,85 @@ __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
   }
 }
 
+// The same fold through staged tiles (16-byte packs only): the block stages
+// M runs of 64 packs of every rank in LDS, each thread folds whole 32-bit
+// words of the tile's columns over ranks c+1, ..., c (the hops above, on the
+// word's one or two elements), and the results go to every rank (ALL) or to
+// rank c.
+template <ar_dtype_t DT, ar_op_t OP, bool ALL, int NMAX>
+__global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
+  using T = typename Elem<DT>::T;
+  constexpr int K = 16 / sizeof(T);
+  constexpr int M = stage_runs(NMAX);
+  constexpr int TP = kRun * M;
+  using WP = Pack<T, 4 / sizeof(T)>;
+  using S = Pack<T, 1>;
+  using F = Fold<DT, OP, WP>;
+  extern __shared__ Raw16 stage[];
+
+  const int n = a.n;
+  const int c = blockIdx.y;
+  const uint64_t lo = umin(static_cast<uint64_t>(c) * a.chunk, a.count);
+  const uint64_t hi = umin(lo + a.chunk, a.count);
+  if (lo >= hi) return;
+  const int first = wrap_rank(c + 1, n);
+  const Span s = make_span<K>(lo, hi);
+  Raw16* res = stage + n * TP;
+
+  for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+    const uint64_t tp0 = (s.plo / TP + tile) * TP;
+    if (tp0 >= s.phi || s.plo >= s.phi) break;
+    const StageTile t{tp0, s.plo, s.phi};
+    stage_in<NMAX, M>(a.ptrs, n, t, stage);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int it = static_cast<int>(threadIdx.x) + i * kBlock;
+      const uint64_t col = tp0 + (it >> 2);
+      if (col >= s.plo && col < s.phi) {
+        const StageWord<WP, M> word{reinterpret_cast<const uint32_t*>(stage), it};
+        typename F::A acc = F::widen(word(first));
+        int r = first;
+        for (int k = 1; k < n; ++k) {
+          r = r + 1 == n ? 0 : r + 1;
+          acc = F::combine(F::widen(word(r)), acc);
+        }
+        reinterpret_cast<uint32_t*>(res)[it] = __builtin_bit_cast(uint32_t, F::narrow(acc));
+      }
+    }
+    __syncthreads();
+    // (the next tile's first barrier orders these reads of res before its
+    // fold overwrites them)
+    if (ALL)
+      stage_out<NMAX, M>(a.ptrs, 0, n, t, res);
+    else
+      stage_out<1, M>(a.ptrs, c, c + 1, t, res);
+  }
+
+  if (blockIdx.x == 0 && threadIdx.x < s.scalar_count()) {
+    using FS = Fold<DT, OP, S>;
+    const uint64_t e = s.scalar_index(threadIdx.x);
+    typename FS::A acc = FS::widen(load<S>(a.ptrs.p[first], e));
+    for (int k = 1; k < n; ++k)
+      acc = FS::combine(FS::widen(load<S>(a.ptrs.p[wrap_rank(first + k, n)], e)), acc);
+    const S out = FS::narrow(acc);
+    if (ALL) {
+      for (int r = 0; r < n; ++r) store<S>(a.ptrs.p[r], e, out);
+    } else {
+      store<S>(a.ptrs.p[c], e, out);
+    }
+  }
+}
+
+template <ar_dtype_t DT, ar_op_t OP, bool ALL>
+const void* ring_stage_fn(int n) {
+  if (n <= 2) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 2>);
+  if (n <= 4) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 4>);
+  if (n <= 8) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 8>);
+  if (n <= 16) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 16>);
+  return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, kStageMaxRanks>);
+}
+
 template <ar_dtype_t DT, ar_op_t OP, bool ALL>
 const void* ring_fold_fn(int u, bool vec) {
   if (!vec) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 1, false>);
@@ -113,6 +192,12 @@ const void* ring_fold_fn(int u, bool vec) {
 template <ar_dtype_t DT, ar_op_t OP>
 hipError_t ring_fold_typed(FoldArgs a, bool all, bool vec, hipStream_t stream) {
   constexpr int K = 16 / sizeof(typename Elem<DT>::T);
+  if (vec && stage_fits(a.n)) {
+    a.tiles = stage_tiles_for(a.chunk, K, stage_runs(a.n));
+    const dim3 grid(grid_x(a.tiles), a.n);
+    const void* fn = all ? ring_stage_fn<DT, OP, true>(a.n) : ring_stage_fn<DT, OP, false>(a.n);
+    return launch(fn, grid, a, stream, stage_bytes(a.n));
+  }
   const int u = vec ? pick_unroll(UnrollFor::kFold, a.n) : 1;
   a.tiles = tiles_for(a.chunk, vec ? K : 1, u);
   const dim3 grid(grid_x(a.tiles), a.n);

@@ -144,6 +144,75 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
   }
 }
 
+// The same folds through staged tiles (16-byte packs only): the block stages
+// M runs of 64 packs of every rank in LDS, each thread runs the rounds above
+// on whole 32-bit words of the tile's columns, and the results go to every
+// rank (double tree) or to the root (Reduce).
+template <ar_dtype_t DT, ar_op_t OP, int NMAX>
+__global__ __launch_bounds__(kBlock) void tree_stage_kernel(TreeArgs a) {
+  using T = typename Elem<DT>::T;
+  constexpr int K = 16 / sizeof(T);
+  constexpr int M = stage_runs(NMAX);
+  constexpr int TP = kRun * M;
+  using WP = Pack<T, 4 / sizeof(T)>;
+  using S = Pack<T, 1>;
+  extern __shared__ Raw16 stage[];
+
+  const int n = a.n;
+  const int tree = blockIdx.y;
+  const int root = a.root;
+  const uint64_t lo = (root >= 0 || tree == 0) ? 0 : a.half;
+  const uint64_t hi = (root >= 0 || tree != 0) ? a.count : a.half;
+  if (lo >= hi) return;
+  const Span s = make_span<K>(lo, hi);
+  Raw16* res = stage + n * TP;
+
+  for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+    const uint64_t tp0 = (s.plo / TP + tile) * TP;
+    if (tp0 >= s.phi || s.plo >= s.phi) break;
+    const StageTile t{tp0, s.plo, s.phi};
+    stage_in<NMAX, M>(a.ptrs, n, t, stage);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int it = static_cast<int>(threadIdx.x) + i * kBlock;
+      const uint64_t col = tp0 + (it >> 2);
+      if (col >= s.plo && col < s.phi) {
+        const StageWord<WP, M> word{reinterpret_cast<const uint32_t*>(stage), it};
+        WP v[1];
+        tree_fold_values<DT, OP, NMAX, 1, WP>(n, tree, root,
+                                              [&](int rank, int) { return word(rank); }, v);
+        reinterpret_cast<uint32_t*>(res)[it] = __builtin_bit_cast(uint32_t, v[0]);
+      }
+    }
+    __syncthreads();
+    // (the next tile's first barrier orders these reads of res before its
+    // fold overwrites them)
+    if (root >= 0)
+      stage_out<1, M>(a.ptrs, root, root + 1, t, res);
+    else
+      stage_out<NMAX, M>(a.ptrs, 0, n, t, res);
+  }
+
+  if (blockIdx.x == 0 && threadIdx.x < s.scalar_count()) {
+    const uint64_t e = s.scalar_index(threadIdx.x);
+    S v[1];
+    tree_fold_values<DT, OP, NMAX, 1, S>(
+        n, tree, root, [&](int rank, int) { return load<S>(a.ptrs.p[rank], e); }, v);
+    for (int r = root >= 0 ? root : 0; r < (root >= 0 ? root + 1 : n); ++r)
+      store<S>(a.ptrs.p[r], e, v[0]);
+  }
+}
+
+template <ar_dtype_t DT, ar_op_t OP>
+const void* tree_stage_fn(int n) {
+  if (n <= 2) return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, 2>);
+  if (n <= 4) return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, 4>);
+  if (n <= 8) return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, 8>);
+  if (n <= 16) return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, 16>);
+  return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, kStageMaxRanks>);
+}
+
 template <ar_dtype_t DT, ar_op_t OP, bool VEC>
 const void* tree_fold_fn(int n) {
   if (n <= 8) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 8, VEC>);
@@ -158,7 +227,13 @@ hipError_t tree_fold_typed(const TreeArgs& a, bool vec, hipStream_t stream) {
   TreeArgs b = a;
   // Reduce: one segment, the whole buffer; double tree: tree 0's half, never
   // the shorter one, bounds both segments.
-  b.tiles = tiles_for(a.root >= 0 ? a.count : a.half, vec ? K : 1, kTreeUnroll);
+  const uint64_t longest = a.root >= 0 ? a.count : a.half;
+  if (vec && stage_fits(a.n)) {
+    b.tiles = stage_tiles_for(longest, K, stage_runs(a.n));
+    const dim3 grid(grid_x(b.tiles), a.root >= 0 ? 1 : 2);
+    return launch(tree_stage_fn<DT, OP>(a.n), grid, b, stream, stage_bytes(a.n));
+  }
+  b.tiles = tiles_for(longest, vec ? K : 1, kTreeUnroll);
   const dim3 grid(grid_x(b.tiles), a.root >= 0 ? 1 : 2);
   return launch(vec ? tree_fold_fn<DT, OP, true>(a.n) : tree_fold_fn<DT, OP, false>(a.n), grid, b,
                 stream);
