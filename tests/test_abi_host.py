@@ -295,6 +295,28 @@ def test_allreduce_choice_switches_at_the_model_crossover():
         ar.set_impl(old)
 
 
+def test_default_model_ties_the_fused_ring_and_tree():
+    """The shipped coefficients give the fused ring and the fused double tree
+    one shared fit (same launches, same bytes), so every size up to 32 ranks
+    predicts a tie and the size-based choice runs the ring (above 32 ranks
+    a large fused ring is two launches); under the step implementation the
+    tree wins small messages (fewer launches) and the ring large ones."""
+    assert ar.get_cost_model("ring_allreduce", "fused") == ar.get_cost_model("tree_allreduce", "fused")
+    old = ar.get_impl()
+    try:
+        ar.set_impl("fused")
+        for t in (1, 256, 262_144, 4_194_304, 67_108_864, 300_000_000):
+            for n in (2, 4, 8, 32):
+                assert ar.predict_time("ring_allreduce", "fused", n, t, "float32") == \
+                    ar.predict_time("tree_allreduce", "fused", n, t, "float32")
+                assert ar.allreduce_choice(n, t, "float32") == "ring_allreduce"
+        ar.set_impl("step")
+        assert ar.allreduce_choice(4, 4_194_304, "float32") == "tree_allreduce"
+        assert ar.allreduce_choice(4, 67_108_864, "float32") == "ring_allreduce"
+    finally:
+        ar.set_impl(old)
+
+
 def test_cost_model_arguments_are_validated():
     lib = ar.lib()
     assert lib.ar_set_cost_model(9, 0, 1.0, 1.0) == binding.INVALID_ARGUMENT
@@ -333,3 +355,27 @@ def test_costfit_recovers_known_coefficients():
     for key, (alpha, gbps) in truth.items():
         assert got[key][0] == pytest.approx(alpha, rel=1e-9)
         assert got[key][1] == pytest.approx(gbps, rel=1e-9)
+
+
+def test_costfit_pools_the_fused_ring_and_tree():
+    """The fused ring and tree AllReduce points are fitted together: both get
+    the pooled least-squares coefficients, so the model ties them (and the
+    size-based choice runs the ring); the step pairs stay separate."""
+    from tree_allreduce_algorithms_amd import costfit
+    truth = {("ring_allreduce", "fused"): (6.0, 6000.0), ("tree_allreduce", "fused"): (6.0, 6000.0),
+             ("tree_allreduce", "step"): (3.0, 5000.0)}
+    records = []
+    for (coll, impl), (alpha, gbps) in truth.items():
+        for nbytes in (8_192, 8.4e6, 1.3e8, 2.1e9):
+            launches = 1 if impl == "fused" else 4
+            us = launches * alpha + nbytes / (gbps * 1e3)
+            records.append({"config": {"collective": coll, "impl": impl,
+                                       "timing": "events, Infinity Cache flushed"},
+                            "roofline": {"launches_per_step": launches,
+                                         "algorithmic_bytes_per_call": nbytes,
+                                         "event_ms_mean": us / 1e3 * (1.02 if coll == "tree_allreduce" else 1.0)}})
+    got = costfit.fit(records)
+    assert got[("ring_allreduce", "fused")] == got[("tree_allreduce", "fused")]
+    assert got[("tree_allreduce", "step")][1] == pytest.approx(5000.0 / 1.02, rel=1e-9)
+    sep = costfit.fit(records, pool_fused_allreduce=False)
+    assert sep[("ring_allreduce", "fused")] != sep[("tree_allreduce", "fused")]

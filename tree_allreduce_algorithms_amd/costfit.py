@@ -61,9 +61,27 @@ def fit_one(pts):
     return alpha, 1.0 / inv
 
 
-def fit(records, cache_state="flushed"):
-    """(collective, impl) -> (alpha_us, gbps) for every pair with >= 2 points."""
-    return {k: fit_one(v) for k, v in points(records, cache_state).items() if len(v) >= 2}
+# On one GPU the fused ring and the fused double tree are one launch each that
+# read N inputs and write N outputs per element: the same work in a different
+# fold order.  Measured over the message-size sweep they are within 1-2 % of
+# each other at every size, inside the run-to-run spread, so their points are
+# fitted together and both get the same coefficients.  The model then predicts
+# equal times and ar_allreduce runs the ring (the tie rule); only the step
+# implementation, whose launch counts differ (2(N-1) against 2 ceil(log2 N)),
+# has a real crossover.
+POOLED = (("ring_allreduce", "fused"), ("tree_allreduce", "fused"))
+
+
+def fit(records, cache_state="flushed", pool_fused_allreduce=True):
+    """(collective, impl) -> (alpha_us, gbps) for every pair with >= 2 points;
+    with pool_fused_allreduce the fused ring and tree AllReduce share one fit
+    over their pooled points."""
+    pts = points(records, cache_state)
+    if pool_fused_allreduce and all(k in pts for k in POOLED):
+        pooled = pts[POOLED[0]] + pts[POOLED[1]]
+        for k in POOLED:
+            pts[k] = pooled
+    return {k: fit_one(v) for k, v in pts.items() if len(v) >= 2}
 
 
 def apply(coeffs):

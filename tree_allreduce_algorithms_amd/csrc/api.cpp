@@ -34,26 +34,30 @@ thread_local int t_last_hip_error = 0;
 // Cost model coefficients (alpha_us per launch, gbps of HBM traffic) per
 // collective and implementation.  The AllReduce pairs are the least-squares
 // fit of launches * alpha + bytes / gbps to the N=4 float32 message-size sweep
-// (1 KiB to 256 MiB per rank, Infinity Cache flushed before every call), two
-// runs on two MI355X boxes pooled.  The other collectives were measured at
-// one size each (N=64 x 64 MB per rank; AllToAll N=8 x 128 MiB), which fixes
-// their bandwidth given the AllReduce fit's per-launch alpha (the tree fold's
-// for Reduce, a step launch's for Scatter, Gather and AllToAll).
+// (1 KiB to 256 MiB per rank, Infinity Cache flushed before every call) on
+// one MI355X.  The fused ring and the fused double tree are one launch of the
+// same work each (N reads and N writes per element) and measure within 1-2 %
+// of each other at every size, so their points are fitted together and they
+// share one pair: the model ties them and the ring runs.  The other
+// collectives were measured at one size each (N=64 x 64 MB per rank; AllToAll
+// N=8 x 128 MiB), which fixes their bandwidth given the AllReduce fit's
+// per-launch alpha (the fused one for fused kernels, a ring step's for step
+// launches, Scatter, Gather and AllToAll).
 struct CostCoeff {
   double alpha_us;
   double gbps;
 };
 std::mutex g_cost_mu;
 CostCoeff g_cost[9][2] = {
-    {{6.36, 5823.0}, {3.44, 6635.0}},   // ring AllReduce: fused, step
-    {{6.36, 5956.0}, {3.44, 6548.0}},   // ReduceScatter
-    {{6.36, 5287.0}, {3.44, 7327.0}},   // AllGather
-    {{6.36, 5284.0}, {3.44, 5777.0}},   // Broadcast
-    {{5.85, 5764.0}, {3.19, 6030.0}},   // double-tree AllReduce
-    {{5.85, 5827.0}, {5.85, 5827.0}},   // Reduce (fused either way)
-    {{3.44, 5049.0}, {3.44, 5049.0}},   // Scatter (one step either way)
-    {{3.44, 5014.0}, {3.44, 5014.0}},   // Gather (one step either way)
-    {{3.44, 5845.0}, {3.44, 5845.0}},   // AllToAll (one kernel either way)
+    {{6.89, 6417.0}, {3.48, 6684.0}},   // ring AllReduce: fused, step
+    {{6.89, 5971.0}, {3.48, 6551.0}},   // ReduceScatter
+    {{6.89, 5400.0}, {3.48, 7450.0}},   // AllGather
+    {{6.89, 5416.0}, {3.48, 5839.0}},   // Broadcast
+    {{6.89, 6417.0}, {3.23, 5996.0}},   // double-tree AllReduce
+    {{6.89, 5651.0}, {6.89, 5651.0}},   // Reduce (fused either way)
+    {{3.48, 5058.0}, {3.48, 5058.0}},   // Scatter (one step either way)
+    {{3.48, 4982.0}, {3.48, 4982.0}},   // Gather (one step either way)
+    {{3.48, 5866.0}, {3.48, 5866.0}},   // AllToAll (one kernel either way)
 };
 
 bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_ALLTOALL; }
