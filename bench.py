@@ -61,16 +61,13 @@ DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
 MAX_CALLS = 35
 COLLECTIVES = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce",
                "allreduce", "reduce", "scatter", "gather", "alltoall"]
-STAGE_MAX_RANKS = 32   # the folds run through LDS-staged tiles for 2 to 32 ranks
-
-
 def kernel_name(collective, impl, n):
-    """The kernel that dominates one call (16-byte aligned rank buffers)."""
-    staged = 2 <= n <= STAGE_MAX_RANKS
+    """The kernel that dominates one call (16-byte aligned rank buffers): the
+    folds run through LDS-staged tiles for every N >= 2."""
     if collective in ("ring_allreduce", "reduce_scatter") and impl == "fused":
-        return "ring_stage_kernel" if staged else "ring_fold_kernel"
+        return "ring_stage_kernel"
     if collective == "tree_allreduce" and impl == "fused" or collective == "reduce":
-        return "tree_stage_kernel" if staged else "tree_fold_kernel"
+        return "tree_stage_kernel"
     if collective in ("allgather", "broadcast") and impl == "fused":
         return "fanout_kernel"
     if collective == "alltoall":

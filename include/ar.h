@@ -128,8 +128,9 @@ typedef enum {
 
 /* How a collective is executed; results are bit-identical either way.
  *   AR_IMPL_FUSED  one pass: every element's N inputs are read once, folded
- *                  in the schedule's order in registers, and the result is
- *                  written once per destination rank.
+ *                  in the schedule's order (tiles staged through LDS, the
+ *                  partials in registers), and the result is written once
+ *                  per destination rank.
  *   AR_IMPL_STEP   the schedule literally: one kernel launch per ring step or
  *                  tree round, each applying all of that step's transfers. */
 typedef enum { AR_IMPL_FUSED = 0, AR_IMPL_STEP = 1 } ar_impl_t;

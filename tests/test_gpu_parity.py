@@ -883,9 +883,10 @@ def test_rank_buffers_match_the_free_functions():
 
 @pytest.mark.parametrize("unroll", ["1", "2", "4"])
 def test_unroll_override_is_bit_identical(unroll):
-    """AR_TUNE_UNROLL only regroups packs: forced to 1, 2 or 4 packs per lane,
-    the fold and fan-out kernels give the oracle's results bit for bit.  The
-    value is read once per process, so each runs in a child process."""
+    """AR_TUNE_UNROLL only regroups the fan-out's packs: forced to 1, 2 or 4
+    packs per lane, the fan-out (and the folds, which ignore it) give the
+    oracle's results bit for bit.  The value is read once per process, so
+    each runs in a child process."""
     import subprocess
     announce(f"unroll override {unroll} (child process)")
     env = dict(os.environ, AR_TUNE_UNROLL=unroll)

@@ -1,11 +1,11 @@
 """Worker for test_unroll_override_is_bit_identical (not collected by pytest).
 
 The library reads AR_TUNE_UNROLL once per process, so each forced value runs
-in a process of its own: this script checks the fused ring fold
-(ReduceScatter, ring AllReduce) and the fan-out copy (AllGather, Broadcast)
-against the oracle, every element, on ragged shapes whose default pack
-grouping differs from the forced one.  Exit status 0 when every result
-matches.
+in a process of its own: this script checks the fan-out copy (AllGather,
+Broadcast), whose pack grouping the variable forces, and the fused ring fold
+(ReduceScatter, ring AllReduce, which must not depend on it) against the
+oracle, every element, on ragged shapes whose default pack grouping differs
+from the forced one.  Exit status 0 when every result matches.
 """
 
 import os

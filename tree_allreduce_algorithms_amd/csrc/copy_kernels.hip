@@ -148,7 +148,7 @@ hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t
   a.n = n;
   a.root = from_root ? root : -1;
   const int pack = vec ? static_cast<int>(16 / itemsize(dtype)) : 1;
-  const int u = vec ? pick_unroll(UnrollFor::kFanout, n) : 1;
+  const int u = vec ? pick_fanout_unroll(n) : 1;
   a.tiles = tiles_for(a.chunk, pack, u);
   const dim3 grid(grid_x(a.tiles), n);
   const void* fn = itemsize(dtype) == 2 ? fanout_fn<uint16_t>(u, vec) : fanout_fn<uint32_t>(u, vec);

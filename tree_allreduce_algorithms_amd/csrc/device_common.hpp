@@ -340,9 +340,16 @@ constexpr int kStageWaves = kBlock / 64;
 // per wave.
 constexpr int stage_runs(int n) { return n <= 2 ? 4 : n <= 4 ? 2 : 1; }
 
-// LDS bytes of a staged tile: n rows of M runs, plus M runs of results.
+// Ranks staged at once.  A fold of more ranks stages them in groups of this
+// many, in the fold's order, each thread carrying its partial in registers
+// from group to group.
+constexpr int kStageGroup = 32;
+constexpr int stage_slots(int n) { return n < kStageGroup ? n : kStageGroup; }
+
+// LDS bytes of a staged tile: one group of rows of M runs, plus M runs of
+// results.
 inline size_t stage_bytes(int n) {
-  return static_cast<size_t>(n + 1) * stage_runs(n) * kRun * 16;
+  return static_cast<size_t>(stage_slots(n) + 1) * stage_runs(n) * kRun * 16;
 }
 
 // A value the whole wave agrees on, kept in a scalar register.
@@ -363,18 +370,30 @@ struct StageTile {
   __device__ uint64_t safe(int m) const { return live(m) ? pack(m) : plo; }
 };
 
-// Phase 1 for a wave holding exactly C (rank, run) pairs: all C loads are
+// Which rank fills LDS slot s of a staged tile.
+struct SlotIsRank {   // slot s holds rank s
+  __device__ int operator()(int s) const { return s; }
+};
+struct RingSlot {     // slot s holds ring position base + s of the fold that starts at `first`
+  int first, base, n;
+  __device__ int operator()(int s) const {
+    const int r = first + base + s;
+    return r >= n ? r - n : r;
+  }
+};
+
+// Phase 1 for a wave holding exactly C (slot, run) pairs: all C loads are
 // issued before the first is waited for, with no lane-dependent branch
 // between them.
-template <int M, int C>
+template <int M, int C, class RankOf>
 __device__ __forceinline__ void stage_rows(const RankPtrs& ptrs, int w, const StageTile& t,
-                                           Raw16* stage) {
+                                           const RankOf& rank_of, Raw16* stage) {
   const int lane = threadIdx.x & 63;
   Raw16 v[C];
 #pragma unroll
   for (int i = 0; i < C; ++i) {
     const int q = w + i * kStageWaves;
-    v[i] = __builtin_nontemporal_load(reinterpret_cast<const Raw16*>(ptrs.p[q / M]) +
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const Raw16*>(ptrs.p[rank_of(q / M)]) +
                                       t.safe(q % M));
   }
 #pragma unroll
@@ -384,27 +403,29 @@ __device__ __forceinline__ void stage_rows(const RankPtrs& ptrs, int w, const St
   }
 }
 
-template <int M, int C>
+template <int M, int C, class RankOf>
 __device__ __forceinline__ void stage_rows_upto(int count, const RankPtrs& ptrs, int w,
-                                                const StageTile& t, Raw16* stage) {
+                                                const StageTile& t, const RankOf& rank_of,
+                                                Raw16* stage) {
   if constexpr (C > 0) {
     if (count == C)
-      stage_rows<M, C>(ptrs, w, t, stage);
+      stage_rows<M, C>(ptrs, w, t, rank_of, stage);
     else
-      stage_rows_upto<M, C - 1>(count, ptrs, w, t, stage);
+      stage_rows_upto<M, C - 1>(count, ptrs, w, t, rank_of, stage);
   }
 }
 
-// Phase 1: every (rank, run) pair of ranks [0, n), n <= NMAX, into LDS slot
-// rank * M + run.  The segment must hold at least one whole pack.
-template <int NMAX, int M>
-__device__ __forceinline__ void stage_in(const RankPtrs& ptrs, int n, const StageTile& t,
-                                         Raw16* stage) {
-  constexpr int R = (NMAX * M + kStageWaves - 1) / kStageWaves;
+// Phase 1: every (slot, run) pair of slots [0, slots), slots <= SMAX, into
+// LDS slot * M + run, slot s read from rank rank_of(s).  The segment must hold
+// at least one whole pack.
+template <int SMAX, int M, class RankOf>
+__device__ __forceinline__ void stage_in(const RankPtrs& ptrs, int slots, const StageTile& t,
+                                         const RankOf& rank_of, Raw16* stage) {
+  constexpr int R = (SMAX * M + kStageWaves - 1) / kStageWaves;
   const int w = wave_uniform(threadIdx.x >> 6);
-  const int pairs = n * M;
+  const int pairs = slots * M;
   const int count = w < pairs ? (pairs - w + kStageWaves - 1) / kStageWaves : 0;
-  stage_rows_upto<M, R>(count, ptrs, w, t, stage);
+  stage_rows_upto<M, R>(count, ptrs, w, t, rank_of, stage);
 }
 
 // Phase 3: result run m (res[64 m, 64 m + 64)) into run m of ranks [r0, r1),
@@ -452,25 +473,20 @@ inline uint64_t tiles_for(uint64_t max_elems, int pack, int unroll) {
   return (packs + per_tile - 1) / per_tile + 1;
 }
 
-// Packs per lane per tile.  Measured on gfx950 by alternating both choices in
-// one process over about 10 GB of rank buffers.  The ring fold is 5 % faster
-// with one pack per lane at N = 4 and 8.  Above N = 8 two packs are faster
-// for the AllReduce at N = 12, 16 and 32 (2-5 %) and tie at N = 64; for the
-// ReduceScatter they are 3.5 % faster at N = 64 and within 2 % at N = 16 and
-// 32.  The fan-out copy is best at four packs for N <= 8 and two above.
-// AR_TUNE_UNROLL (1, 2 or 4), read at the first launch, overrides both for
-// measurements; it changes nothing but the pack grouping, never any element's
-// arithmetic.
-enum class UnrollFor { kFold, kFanout };
-
-inline int pick_unroll(UnrollFor kind, int n) {
+// Packs per lane per tile of the fan-out copy.  Measured on gfx950 by
+// alternating both choices in one process over about 10 GB of rank buffers:
+// four packs are best for N <= 8 and two above (one pack is 11 % slower at
+// N = 64).  AR_TUNE_UNROLL (1, 2 or 4), read at the first launch, overrides
+// the choice for measurements; it changes nothing but the pack grouping,
+// never any element's arithmetic.  (The folds stage their tiles through LDS
+// and have no such choice.)
+inline int pick_fanout_unroll(int n) {
   static const int forced = [] {
     const char* v = std::getenv("AR_TUNE_UNROLL");
     const int u = v != nullptr ? std::atoi(v) : 0;
     return (u == 1 || u == 2 || u == 4) ? u : 0;
   }();
   if (forced != 0) return forced;
-  if (kind == UnrollFor::kFold) return n <= 8 ? 1 : 2;
   return n <= 8 ? 4 : 2;
 }
 
@@ -486,14 +502,14 @@ hipError_t launch(const void* fn, dim3 grid, const Args& args, hipStream_t strea
   return hipLaunchKernel(fn, grid, dim3(kBlock), kargs, lds_bytes, stream);
 }
 
-// The folds use staged tiles for 2 to 32 ranks (at most 33 KiB of LDS per
+// The folds use staged tiles from 2 ranks up (at most 33 KiB of LDS per
 // block).  Measured on gfx950 against folding in registers, float32, about
-// 9.6 GB of inputs: ring AllReduce 7-10 % faster at N = 5 to 16 and 3 %
-// at 32, ReduceScatter 12 % at 8 and 16, double tree and Reduce 5-12 % at
-// 3 to 16; within placement noise (+-5 %) at N = 2 to 4.  Above 32 ranks a
-// tile's LDS would cap the blocks per CU; the register fold stays.
-constexpr int kStageMaxRanks = 32;
-inline bool stage_fits(int n) { return n >= 2 && n <= kStageMaxRanks; }
+// 9.6 GB of inputs: ring AllReduce 7-10 % faster at N = 5 to 16,
+// ReduceScatter 12 % at 8 and 16 and 6-8 % at 40 to 64 (two groups), double
+// tree and Reduce 5-12 % at 3 to 16; within placement noise (+-5 %) at N = 2
+// to 4.
+inline bool stage_ring(int n) { return n >= 2; }
+inline bool stage_tree(int n) { return n >= 2; }
 
 // Tiles of the staged grid (M runs each, anchored at pack 0) that a segment
 // of at most max_elems elements touches.

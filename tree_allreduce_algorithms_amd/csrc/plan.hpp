@@ -80,14 +80,13 @@ uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t co
 // fold that stores into all N ranks.  Both give the same bits: AllReduce is
 // AllGather after ReduceScatter [Lecture 09 section 3.9], and the
 // ReduceScatter leaves exactly the value the one-pass fold stores.  Measured
-// on gfx950 (in-process A/B, float32) against the register fold that serves
-// more than 32 ranks, the two phases win although they move T * s more
-// bytes: one phase mostly reads and the other mostly writes, while the
-// one-pass fold mixes a read and a write stream per rank.  With 9.6 GB of
-// inputs: N = 48 +6.5 %, 64 +8 %; with 256 MiB: N = 64 +17 %.  With 64 MiB
-// (N = 64, Infinity-Cache resident) the one-pass fold is 13 % faster.  Up to
-// 32 ranks the one-pass fold runs through LDS-staged tiles, which beat the
-// two phases at 9.6 GB (N = 32: 5-8 %), so the split starts at 33 ranks.
+// on gfx950 (in-process A/B, float32, both folds through LDS-staged tiles),
+// the two phases win above 32 ranks although they move T * s more bytes: the
+// one-pass fold's stores to every rank become deep per-wave store bursts
+// there.  With 9.6 GB of inputs: N = 33 +1 %, 40 +2 %, 48 +3 %, 64 +5 %; with
+// 512 MiB (N = 64) +19 %.  At 32 ranks and 9.6 GB the one-pass fold is 5-8 %
+// faster, so the split starts at 33 ranks; below 256 MiB of inputs (Infinity
+// Cache resident) one launch stays.
 bool ring_allreduce_split(int n, uint64_t count, size_t isz);
 
 // Validation shared by every collective call.  `op` < 0 means "not used",

@@ -22,11 +22,14 @@ struct FoldArgs {
   int n;
 };
 
-// U: packs per lane per tile.  ALL: store into every rank (AllReduce) or only
-// into the chunk's owner (ReduceScatter).  VEC: 16-byte packs, else one
-// element per pack.
-template <ar_dtype_t DT, ar_op_t OP, bool ALL, int U, bool VEC>
+// The fold in registers, one element per lane: the path for rank buffers
+// aligned only to the element size (16-byte aligned buffers take the staged
+// kernel below).  ALL: store into every rank (AllReduce) or only into the
+// chunk's owner (ReduceScatter).
+template <ar_dtype_t DT, ar_op_t OP, bool ALL>
 __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
+  constexpr int U = 1;
+  constexpr bool VEC = false;
   using T = typename Elem<DT>::T;
   constexpr int K = PackOf<T, VEC>::K;
   constexpr int B = kFoldBatch;
@@ -102,17 +105,19 @@ __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
   }
 }
 
-// The same fold through staged tiles (16-byte packs only): the block stages
-// M runs of 64 packs of every rank in LDS, each thread folds whole 32-bit
-// words of the tile's columns over ranks c+1, ..., c (the hops above, on the
-// word's one or two elements), and the results go to every rank (ALL) or to
-// rank c.
+// The same fold through staged tiles (16-byte packs only).  LDS slot s holds
+// ring position s of the fold (rank c+1+s), M runs of 64 packs each; each
+// thread folds whole 32-bit words of the tile's columns (the hops above, on
+// the word's one or two elements) in slot order, and the results go to every
+// rank (ALL) or to rank c.  More than kStageGroup ranks are staged in groups
+// of equal size, each thread carrying its partials in registers.
 template <ar_dtype_t DT, ar_op_t OP, bool ALL, int NMAX>
 __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int K = 16 / sizeof(T);
   constexpr int M = stage_runs(NMAX);
   constexpr int TP = kRun * M;
+  constexpr int G = stage_slots(NMAX);
   using WP = Pack<T, 4 / sizeof(T)>;
   using S = Pack<T, 1>;
   using F = Fold<DT, OP, WP>;
@@ -125,30 +130,40 @@ __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
   if (lo >= hi) return;
   const int first = wrap_rank(c + 1, n);
   const Span s = make_span<K>(lo, hi);
-  Raw16* res = stage + n * TP;
+  Raw16* res = stage + stage_slots(n) * TP;   // the layout stage_bytes(n) allocates
+  // groups of equal size (at most G): 33 ranks go as 17 + 16, not 32 + 1
+  const int groups = (n + G - 1) / G;
+  const int gsize = (n + groups - 1) / groups;
 
   for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
     const uint64_t tp0 = (s.plo / TP + tile) * TP;
     if (tp0 >= s.phi || s.plo >= s.phi) break;
     const StageTile t{tp0, s.plo, s.phi};
-    stage_in<NMAX, M>(a.ptrs, n, t, stage);
-    __syncthreads();
+    typename F::A acc[M];
+    for (int g0 = 0; g0 < n; g0 += gsize) {
+      const int slots = n - g0 < gsize ? n - g0 : gsize;
+      stage_in<G, M>(a.ptrs, slots, t, RingSlot{first, g0, n}, stage);
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const int it = static_cast<int>(threadIdx.x) + i * kBlock;
-      const uint64_t col = tp0 + (it >> 2);
-      if (col >= s.plo && col < s.phi) {
-        const StageWord<WP, M> word{reinterpret_cast<const uint32_t*>(stage), it};
-        typename F::A acc = F::widen(word(first));
-        int r = first;
-        for (int k = 1; k < n; ++k) {
-          r = r + 1 == n ? 0 : r + 1;
-          acc = F::combine(F::widen(word(r)), acc);
+      for (int i = 0; i < M; ++i) {
+        const int it = static_cast<int>(threadIdx.x) + i * kBlock;
+        const uint64_t col = tp0 + (it >> 2);
+        if (col >= s.plo && col < s.phi) {
+          const StageWord<WP, M> word{reinterpret_cast<const uint32_t*>(stage), it};
+          int k = 0;
+          if (g0 == 0) {
+            acc[i] = F::widen(word(0));
+            k = 1;
+          }
+          for (; k < slots; ++k) acc[i] = F::combine(F::widen(word(k)), acc[i]);
+          if (g0 + slots == n)
+            reinterpret_cast<uint32_t*>(res)[it] = __builtin_bit_cast(uint32_t, F::narrow(acc[i]));
         }
-        reinterpret_cast<uint32_t*>(res)[it] = __builtin_bit_cast(uint32_t, F::narrow(acc));
       }
+      // orders this group's reads of the stage before the next group's
+      // loads overwrite it, and the results before the stores read them
+      __syncthreads();
     }
-    __syncthreads();
     // (the next tile's first barrier orders these reads of res before its
     // fold overwrites them)
     if (ALL)
@@ -178,30 +193,23 @@ const void* ring_stage_fn(int n) {
   if (n <= 4) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 4>);
   if (n <= 8) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 8>);
   if (n <= 16) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 16>);
-  return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, kStageMaxRanks>);
-}
-
-template <ar_dtype_t DT, ar_op_t OP, bool ALL>
-const void* ring_fold_fn(int u, bool vec) {
-  if (!vec) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 1, false>);
-  if (u == 4) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 4, true>);
-  if (u == 2) return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 2, true>);
-  return reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, ALL, 1, true>);
+  if (n <= 32) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 32>);
+  return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, AR_MAX_RANKS>);
 }
 
 template <ar_dtype_t DT, ar_op_t OP>
 hipError_t ring_fold_typed(FoldArgs a, bool all, bool vec, hipStream_t stream) {
   constexpr int K = 16 / sizeof(typename Elem<DT>::T);
-  if (vec && stage_fits(a.n)) {
+  if (vec && stage_ring(a.n)) {
     a.tiles = stage_tiles_for(a.chunk, K, stage_runs(a.n));
     const dim3 grid(grid_x(a.tiles), a.n);
     const void* fn = all ? ring_stage_fn<DT, OP, true>(a.n) : ring_stage_fn<DT, OP, false>(a.n);
     return launch(fn, grid, a, stream, stage_bytes(a.n));
   }
-  const int u = vec ? pick_unroll(UnrollFor::kFold, a.n) : 1;
-  a.tiles = tiles_for(a.chunk, vec ? K : 1, u);
+  a.tiles = tiles_for(a.chunk, 1, 1);
   const dim3 grid(grid_x(a.tiles), a.n);
-  return launch(all ? ring_fold_fn<DT, OP, true>(u, vec) : ring_fold_fn<DT, OP, false>(u, vec),
+  return launch(all ? reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, true>)
+                    : reinterpret_cast<const void*>(&ring_fold_kernel<DT, OP, false>),
                 grid, a, stream);
 }
 

@@ -32,21 +32,71 @@ struct TreeArgs {
   int root;   // >= 0: Reduce to `root` (one tree over the whole buffer)
 };
 
-constexpr int kTreeUnroll = 1;   // measured 2-4 % faster than 2 at N = 4, 8 and 64
 constexpr int kTreeBatch = 8;
 
 constexpr int ilog2_ceil(int v) { return v <= 1 ? 0 : 1 + ilog2_ceil((v + 1) / 2); }
 
-// Folds U packs of every role of one tree; load(rank, u) loads rank's pack u.
-// Roles map to ranks as role == rank (tree 0), N-1-role (tree 1) or, for a
-// Reduce, (role + root) mod N.
-template <ar_dtype_t DT, ar_op_t OP, int NMAX, int U, class P, class Load>
-__device__ __forceinline__ void tree_fold_values(int n, int tree, int root, const Load& load,
-                                                 P out[U]) {
+// The rank that plays `role` in tree 0 (role == rank), tree 1 (N-1-role) or,
+// for a Reduce (root >= 0), the tree on roles (rank - root) mod N.
+__device__ __forceinline__ int tree_role_rank(int role, int tree, int root, int n) {
+  return root >= 0 ? wrap_rank(role + root, n) : (tree == 0 ? role : n - 1 - role);
+}
+
+// The binary counter over roles 0, 1, ..., N-1 described above, for U values
+// per role.  push() takes the roles in order; its role must be a compile-time
+// constant after unrolling at the call site, so that the bit tests and the
+// slot indices resolve at compile time and the slots stay in registers.
+template <ar_dtype_t DT, ar_op_t OP, int NMAX, int U, class P> struct TreeCounter {
   using F = Fold<DT, OP, P>;
   using A = typename F::A;
-  constexpr int L = ilog2_ceil(NMAX) + 1;
+  static constexpr int L = ilog2_ceil(NMAX) + 1;
   A slot[L][U];
+
+  __device__ __forceinline__ void push(int q, const P (&in)[U]) {
+    A cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = F::widen(in[u]);
+    int l = 0;
+#pragma unroll
+    for (int bit = 0; bit < L; ++bit) {
+      if (((q >> bit) & 1) == 0) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = F::combine(slot[bit][u], cur[u]);
+      l = bit + 1;
+    }
+#pragma unroll
+    for (int ll = 0; ll < L; ++ll)
+      if (ll == l) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) slot[ll][u] = cur[u];
+      }
+  }
+
+  // After roles 0..n-1: the occupied slots are the set bits of n; combine
+  // them from the smallest block upward, each larger block receiving.
+  __device__ __forceinline__ void finish(int n, P (&out)[U]) const {
+    A res[U];
+    bool have = false;
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+      if ((n >> l) & 1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) res[u] = have ? F::combine(slot[l][u], res[u]) : slot[l][u];
+        have = true;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) out[u] = F::narrow(res[u]);
+  }
+};
+
+// Folds U packs of every role of one tree; load(rank, u) loads rank's pack u.
+// Roles are loaded in batches of kTreeBatch so that many loads are in flight
+// before the first combine.
+template <ar_dtype_t DT, ar_op_t OP, int NMAX, int U, class P, class Load>
+__device__ __forceinline__ void tree_fold_values(int n, int tree, int root, const Load& load,
+                                                 P (&out)[U]) {
+  TreeCounter<DT, OP, NMAX, U, P> tc;
 #pragma unroll
   for (int q0 = 0; q0 < NMAX; q0 += kTreeBatch) {
     if (q0 >= n) break;
@@ -55,7 +105,7 @@ __device__ __forceinline__ void tree_fold_values(int n, int tree, int root, cons
     for (int j = 0; j < kTreeBatch; ++j) {
       const int q = q0 + j;
       if (q < n) {
-        const int rank = root >= 0 ? wrap_rank(q + root, n) : (tree == 0 ? q : n - 1 - q);
+        const int rank = tree_role_rank(q, tree, root, n);
 #pragma unroll
         for (int u = 0; u < U; ++u) in[j][u] = load(rank, u);
       }
@@ -63,46 +113,21 @@ __device__ __forceinline__ void tree_fold_values(int n, int tree, int root, cons
 #pragma unroll
     for (int j = 0; j < kTreeBatch; ++j) {
       const int q = q0 + j;   // compile-time after unrolling
-      if (q < n) {
-        A cur[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = F::widen(in[j][u]);
-        int l = 0;
-#pragma unroll
-        for (int bit = 0; bit < L; ++bit) {
-          if (((q >> bit) & 1) == 0) break;
-#pragma unroll
-          for (int u = 0; u < U; ++u) cur[u] = F::combine(slot[bit][u], cur[u]);
-          l = bit + 1;
-        }
-#pragma unroll
-        for (int ll = 0; ll < L; ++ll)
-          if (ll == l) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) slot[ll][u] = cur[u];
-          }
-      }
+      if (q < n) tc.push(q, in[j]);
     }
   }
-  A res[U];
-  bool have = false;
-#pragma unroll
-  for (int l = 0; l < L; ++l) {
-    if ((n >> l) & 1) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) res[u] = have ? F::combine(slot[l][u], res[u]) : slot[l][u];
-      have = true;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) out[u] = F::narrow(res[u]);
+  tc.finish(n, out);
 }
 
-template <ar_dtype_t DT, ar_op_t OP, int NMAX, bool VEC>
+// The folds in registers, one element per lane: the path for rank buffers
+// aligned only to the element size (16-byte aligned buffers take the staged
+// kernel below).
+template <ar_dtype_t DT, ar_op_t OP, int NMAX>
 __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
+  constexpr bool VEC = false;
+  constexpr int U = 1;
   using T = typename Elem<DT>::T;
   constexpr int K = PackOf<T, VEC>::K;
-  constexpr int U = kTreeUnroll;
   using P = typename PackOf<T, VEC>::P;
   using S = Pack<T, 1>;
 
@@ -144,16 +169,24 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
   }
 }
 
+// Slot s of a staged tree group holds role base + s.
+struct TreeSlot {
+  int base, tree, root, n;
+  __device__ int operator()(int s) const { return tree_role_rank(base + s, tree, root, n); }
+};
+
 // The same folds through staged tiles (16-byte packs only): the block stages
-// M runs of 64 packs of every rank in LDS, each thread runs the rounds above
-// on whole 32-bit words of the tile's columns, and the results go to every
-// rank (double tree) or to the root (Reduce).
+// M runs of 64 packs of each role in LDS, a group of kStageGroup roles at a
+// time (roles 0-31, then 32-63), each thread pushes whole 32-bit words of the
+// tile's columns through the counter above in role order, and the results go
+// to every rank (double tree) or to the root (Reduce).
 template <ar_dtype_t DT, ar_op_t OP, int NMAX>
 __global__ __launch_bounds__(kBlock) void tree_stage_kernel(TreeArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int K = 16 / sizeof(T);
   constexpr int M = stage_runs(NMAX);
   constexpr int TP = kRun * M;
+  constexpr int G = stage_slots(NMAX);
   using WP = Pack<T, 4 / sizeof(T)>;
   using S = Pack<T, 1>;
   extern __shared__ Raw16 stage[];
@@ -165,27 +198,41 @@ __global__ __launch_bounds__(kBlock) void tree_stage_kernel(TreeArgs a) {
   const uint64_t hi = (root >= 0 || tree != 0) ? a.count : a.half;
   if (lo >= hi) return;
   const Span s = make_span<K>(lo, hi);
-  Raw16* res = stage + n * TP;
+  Raw16* res = stage + stage_slots(n) * TP;   // the layout stage_bytes(n) allocates
 
   for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
     const uint64_t tp0 = (s.plo / TP + tile) * TP;
     if (tp0 >= s.phi || s.plo >= s.phi) break;
     const StageTile t{tp0, s.plo, s.phi};
-    stage_in<NMAX, M>(a.ptrs, n, t, stage);
-    __syncthreads();
+    TreeCounter<DT, OP, NMAX, 1, WP> tc[M];
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const int it = static_cast<int>(threadIdx.x) + i * kBlock;
-      const uint64_t col = tp0 + (it >> 2);
-      if (col >= s.plo && col < s.phi) {
-        const StageWord<WP, M> word{reinterpret_cast<const uint32_t*>(stage), it};
-        WP v[1];
-        tree_fold_values<DT, OP, NMAX, 1, WP>(n, tree, root,
-                                              [&](int rank, int) { return word(rank); }, v);
-        reinterpret_cast<uint32_t*>(res)[it] = __builtin_bit_cast(uint32_t, v[0]);
+    for (int g0 = 0; g0 < NMAX; g0 += G) {
+      if (g0 >= n) break;
+      const int slots = n - g0 < G ? n - g0 : G;
+      stage_in<G, M>(a.ptrs, slots, t, TreeSlot{g0, tree, root, n}, stage);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int it = static_cast<int>(threadIdx.x) + i * kBlock;
+        const uint64_t col = tp0 + (it >> 2);
+        if (col >= s.plo && col < s.phi) {
+          const StageWord<WP, M> word{reinterpret_cast<const uint32_t*>(stage), it};
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const WP v[1] = {word(j)};
+            if (g0 + j < n) tc[i].push(g0 + j, v);   // role compile-time after unrolling
+          }
+          if (g0 + slots == n) {
+            WP out[1];
+            tc[i].finish(n, out);
+            reinterpret_cast<uint32_t*>(res)[it] = __builtin_bit_cast(uint32_t, out[0]);
+          }
+        }
       }
+      // orders this group's reads of the stage before the next group's
+      // loads overwrite it, and the results before the stores read them
+      __syncthreads();
     }
-    __syncthreads();
     // (the next tile's first barrier orders these reads of res before its
     // fold overwrites them)
     if (root >= 0)
@@ -210,15 +257,16 @@ const void* tree_stage_fn(int n) {
   if (n <= 4) return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, 4>);
   if (n <= 8) return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, 8>);
   if (n <= 16) return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, 16>);
-  return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, kStageMaxRanks>);
+  if (n <= 32) return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, 32>);
+  return reinterpret_cast<const void*>(&tree_stage_kernel<DT, OP, AR_MAX_RANKS>);
 }
 
-template <ar_dtype_t DT, ar_op_t OP, bool VEC>
+template <ar_dtype_t DT, ar_op_t OP>
 const void* tree_fold_fn(int n) {
-  if (n <= 8) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 8, VEC>);
-  if (n <= 16) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 16, VEC>);
-  if (n <= 32) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 32, VEC>);
-  return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, AR_MAX_RANKS, VEC>);
+  if (n <= 8) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 8>);
+  if (n <= 16) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 16>);
+  if (n <= 32) return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, 32>);
+  return reinterpret_cast<const void*>(&tree_fold_kernel<DT, OP, AR_MAX_RANKS>);
 }
 
 template <ar_dtype_t DT, ar_op_t OP>
@@ -228,15 +276,14 @@ hipError_t tree_fold_typed(const TreeArgs& a, bool vec, hipStream_t stream) {
   // Reduce: one segment, the whole buffer; double tree: tree 0's half, never
   // the shorter one, bounds both segments.
   const uint64_t longest = a.root >= 0 ? a.count : a.half;
-  if (vec && stage_fits(a.n)) {
+  if (vec && stage_tree(a.n)) {
     b.tiles = stage_tiles_for(longest, K, stage_runs(a.n));
     const dim3 grid(grid_x(b.tiles), a.root >= 0 ? 1 : 2);
     return launch(tree_stage_fn<DT, OP>(a.n), grid, b, stream, stage_bytes(a.n));
   }
-  b.tiles = tiles_for(longest, vec ? K : 1, kTreeUnroll);
+  b.tiles = tiles_for(longest, 1, 1);
   const dim3 grid(grid_x(b.tiles), a.root >= 0 ? 1 : 2);
-  return launch(vec ? tree_fold_fn<DT, OP, true>(a.n) : tree_fold_fn<DT, OP, false>(a.n), grid, b,
-                stream);
+  return launch(tree_fold_fn<DT, OP>(a.n), grid, b, stream);
 }
 
 }  // namespace
