@@ -391,6 +391,8 @@ def run_one(args):
             "event_ms_mean": round(launch_ms, 4),
             "event_ms_median": round(sorted(event_ms)[len(event_ms) // 2], 4),
             "event_ms_min": round(min(event_ms), 4),
+            "event_ms_p90": round(sorted(event_ms)[min(len(event_ms) - 1,
+                                                       int(0.9 * len(event_ms)))], 4),
             "event_ms_max": round(max(event_ms), 4),
         },
         "outputs_finite": finite,
