@@ -31,9 +31,13 @@ int32 brute force, hand-derived order-revealing fp32 examples, the worked
 examples the pages print, an independently written 0-based schedule from the
 Lecture 09 lab / Chapter 4 pseudo-code on rotated ranks, the exactly rounded
 sum (``math.fsum``) within the recursive-summation bound, the pages' byte and
-step counts, and torch's CPU bfloat16 conversion.  Parity unpinned by the pages
-(pinned only by brute force, coverage and byte invariants): the ragged chunk
-layout and the double-tree shape, both of which the pages leave open.
+step counts, and torch's CPU bfloat16 conversion.  Two readings are this
+package's own because the pages leave them open: the ragged chunk layout and
+the double-tree shape and split.  No page value can fix them; the oracle's
+implementation of each is pinned independently (chunks covering every element
+once in rank order, int32 brute force on ragged shapes, the binomial recursion
+evaluated directly on each half, the pages' n=3 and n=4 pairing examples and
+the cost table's per-rank bytes).
 """
 
 from .numerics import (  # noqa: F401
