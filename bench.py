@@ -8,8 +8,10 @@ MI355X, through the C ABI of libar.so.
 
 One "step" is one collective call over the whole workload (every rank buffer
 already resident in HBM).  W untimed calls, then K timed calls bracketed by
-torch.cuda.synchronize(); each call is also bracketed by HIP events recorded
-on the stream the library launches on.  Rank 0 prints one JSON line.
+torch.cuda.synchronize(); HIP events recorded on the stream the library
+launches on bracket each call (or, for calls under 1 GiB of traffic run
+back to back, the whole group of K calls, whose event time is then spread
+evenly over them).  Rank 0 prints one JSON line.
 
 The collectives work in place, so step k+1 reduces step k's output: after an
 AllReduce every rank holds the sum, and each further call multiplies the
@@ -321,8 +323,18 @@ def run_one(args):
     for _ in range(args.warmup):
         call(bufs)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Events bracket every call when the Infinity Cache is flushed between
+    # calls (the flush must stay outside them) or when a call moves enough
+    # bytes that recording two events (a few microseconds of host time each)
+    # is noise.  Small calls back to back are bracketed as one group of K
+    # calls instead: per-call events would make the host loop, and with it
+    # the wall time, several times slower than the calls themselves.
+    per_call_events = args.flush_mall or algorithmic_bytes(args.collective if args.collective
+                                                           != "allreduce" else "ring_allreduce",
+                                                           n, t, isz, args.root) >= (1 << 30)
+    nev = args.steps if per_call_events else 1
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
 
     # collect garbage now (earlier runs free large host arrays) and keep the
     # collector out of the timed loop, which small workloads make host-bound
@@ -330,16 +342,25 @@ def run_one(args):
     gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.fill_(float(i))
-        starts[i].record(stream)
-        call(bufs)
-        ends[i].record(stream)
+    if per_call_events:
+        for i in range(args.steps):
+            if flush_buf is not None:
+                flush_buf.fill_(float(i))
+            starts[i].record(stream)
+            call(bufs)
+            ends[i].record(stream)
+    else:
+        starts[0].record(stream)
+        for i in range(args.steps):
+            call(bufs)
+        ends[0].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
-    event_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if per_call_events:
+        event_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    else:   # the group's GPU time spread evenly over its calls
+        event_ms = [starts[0].elapsed_time(ends[0]) / args.steps] * args.steps
     finite = bool(all(torch.isfinite(b).all().item() for b in bufs))
     del flush_buf
 
@@ -388,6 +409,8 @@ def run_one(args):
             "algorithmic_bytes_per_launch": moved if launches == 1 else None,
             "algorithmic_bytes_per_call": moved,
             "launches_per_step": launches,
+            "events": "one pair per call" if per_call_events else
+                      f"one pair around all {args.steps} calls (small calls back to back)",
             "event_ms_mean": round(launch_ms, 4),
             "event_ms_median": round(sorted(event_ms)[len(event_ms) // 2], 4),
             "event_ms_min": round(min(event_ms), 4),
