@@ -111,17 +111,42 @@ KERNEL_FILE = {  # kernel -> the source file that defines it
 }
 
 
+def _code_only(text):
+    """C/C++ source text with comments removed and blank lines dropped, so
+    that a change to comments alone keeps a profile valid."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                                    # string or char literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line.strip())
+
+
 def kernel_source_hash(kernel=None):
-    """sha256 over the device code a kernel is built from: its own source file
-    plus every shared header (all device sources when kernel is None), in
-    name order."""
+    """sha256 over the device code a kernel is built from (comments and blank
+    lines removed): its own source file plus every shared header (all device
+    sources when kernel is None), in name order."""
     csrc = os.path.join(ROOT, "tree_allreduce_algorithms_amd", "csrc")
     own = KERNEL_FILE.get(kernel)
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
         if name.endswith(".hpp") or (name.endswith(".hip") and (own is None or name == own)):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -168,3 +168,13 @@ def test_checker_finds_planted_mismatch_and_all_cores_pass_runs(coll):
     got[1][0 if coll != "reduce_scatter" else 250] += 1.0
     assert bench.run_checker(coll, x, got, w, 0, 256)[2] == 1
     assert bench.time_checker_all_cores(coll, x, w, 0, 256, w.dtype, 3) >= 0
+
+
+def test_kernel_hash_ignores_comments_only():
+    """A profile stays valid across comment edits, and only those: the hash
+    covers the device code with comments and blank lines removed, string
+    and character literals kept as written."""
+    code = 'int a = 1; // note\n/* block\n comment */\nconst char* s = "// not a comment";\n\nchar c = \'/\';\n'
+    assert bench._code_only(code) == 'int a = 1;\nconst char* s = "// not a comment";\nchar c = \'/\';'
+    assert bench._code_only("x = 1;  // a\n") == bench._code_only("x = 1;  // b\n")
+    assert bench._code_only("x = 1;\n") != bench._code_only("x = 2;\n")
