@@ -71,7 +71,7 @@ def kernel_name(collective, impl, n):
     if collective == "tree_allreduce" and impl == "fused" or collective == "reduce":
         return "tree_stage_kernel"
     if collective in ("allgather", "broadcast") and impl == "fused":
-        return "fanout_kernel"
+        return "fanout_group_kernel"
     if collective == "alltoall":
         return "alltoall_kernel"
     return "step_kernel"
@@ -106,7 +106,8 @@ def parse(argv=None):
 KERNEL_FILE = {  # kernel -> the source file that defines it
     "ring_stage_kernel": "ring_kernels.hip", "ring_fold_kernel": "ring_kernels.hip",
     "tree_stage_kernel": "tree_kernels.hip", "tree_fold_kernel": "tree_kernels.hip",
-    "fanout_kernel": "copy_kernels.hip", "alltoall_kernel": "copy_kernels.hip",
+    "fanout_group_kernel": "copy_kernels.hip", "fanout_kernel": "copy_kernels.hip",
+    "alltoall_kernel": "copy_kernels.hip",
     "step_kernel": "step_kernels.hip",
 }
 

@@ -139,7 +139,7 @@ typedef enum { AR_IMPL_FUSED = 0, AR_IMPL_STEP = 1 } ar_impl_t;
  * ReduceScatter then AllGather.  Afterwards every bufs[r] holds, at element
  * i of chunk c, the fold x[c+1][i] (+) ... (+) x[c][i] taken in ring order
  * (each hop: the receiving rank's own value (+) the incoming partial).
- * AR_IMPL_FUSED: one fold storing into every rank; from 33 ranks and 256 MiB
+ * AR_IMPL_FUSED: one fold storing into every rank; from 17 ranks and 384 MiB
  * of inputs (nranks * count * element size) up, the fused ReduceScatter and
  * then the fused AllGather (two launches, the same bits, faster there). */
 ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
@@ -173,7 +173,11 @@ ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t
  * back, each over half the data: tree 0 handles elements [0, ceil(T/2)) with
  * role == rank, tree 1 handles [ceil(T/2), T) with role == N-1-rank.  Reduce
  * round k: role q (q mod 2^(k+1) == 0, q + 2^k < N) stores
- * own (+) value of role q + 2^k.  Every bufs[r] ends with role 0's result. */
+ * own (+) value of role q + 2^k.  Every bufs[r] ends with role 0's result.
+ * AR_IMPL_FUSED: one fold storing into every rank; from 17 ranks and 384 MiB
+ * of inputs up, the two trees' folds stored into their roots (rank 0, rank
+ * N-1) and then both halves fanned out from there (two launches, the same
+ * bits, faster there). */
 ar_status_t ar_tree_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
                               ar_op_t op, hipStream_t stream);
 

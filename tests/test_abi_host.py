@@ -214,8 +214,8 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
     if coll == "alltoall":               # every off-diagonal block read and written once
         return 2 * n * (n - 1) * (t // n) * s
     if impl == "fused" and coll not in ("scatter", "gather"):
-        if coll == "ring_allreduce" and _split(n, t, s):
-            return (2 * n + 1) * t * s     # ReduceScatter (N+1) T s, then AllGather N T s
+        if coll in ("ring_allreduce", "tree_allreduce") and _split(n, t, s):
+            return (2 * n + 1) * t * s     # fold into one rank per element (N+1) T s, then fan-out N T s
         return {"ring_allreduce": 2 * n * t, "tree_allreduce": 2 * n * t,
                 "reduce_scatter": (n + 1) * t, "allgather": n * t, "broadcast": n * t}[coll] * s
     x = [np.zeros(t, np.int32) for _ in range(n)]
@@ -226,9 +226,11 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
 
 
 def _split(n, t, s):
-    """The fused ring AllReduce runs as ReduceScatter then AllGather from 33
-    ranks and 256 MiB of inputs up (the documented rule of ar.h)."""
-    return n >= 33 and n * t * s >= 1 << 28
+    """The fused AllReduces run in two launches from 17 ranks and 384 MiB of
+    inputs up (the documented rule of ar.h): the ring as ReduceScatter then
+    AllGather, the double tree as its folds into the two roots then their
+    fan-out."""
+    return n >= 17 and n * t * s >= 384 << 20
 
 
 @pytest.mark.parametrize("coll", sorted(ORACLE_CALLS))
@@ -238,7 +240,8 @@ def _split(n, t, s):
 def test_predicted_time_is_the_documented_formula(coll, impl, n, t, dtype):
     alpha, gbps = ar.get_cost_model(coll, impl)
     launches = 1 if impl == "fused" or coll in ("reduce", "alltoall") else ar.expected_steps(coll, n)
-    if impl == "fused" and coll == "ring_allreduce" and _split(n, t, 2 if dtype == "bfloat16" else 4):
+    if impl == "fused" and coll in ("ring_allreduce", "tree_allreduce") and \
+            _split(n, t, 2 if dtype == "bfloat16" else 4):
         launches = 2
     if n == 1:
         launches = 0
@@ -246,20 +249,23 @@ def test_predicted_time_is_the_documented_formula(coll, impl, n, t, dtype):
     assert ar.predict_time(coll, impl, n, t, dtype) == pytest.approx(want, rel=1e-12)
 
 
-@pytest.mark.parametrize("n,t,dtype", [(64, 1_048_576, "float32"), (33, 4_194_304, "bfloat16"),
-                                       (32, 100_000_000, "float32"), (33, 2_033_601, "float32"),
-                                       (33, 2_033_600, "float32"), (31, 100_000_000, "float32"),
-                                       (64, 1_048_575, "float32"), (64, 16_777_217, "float32")])
-def test_fused_ring_allreduce_split_is_modelled(n, t, dtype):
-    """From 33 ranks and 256 MiB of inputs the fused ring AllReduce is two
+@pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce"])
+@pytest.mark.parametrize("n,t,dtype", [(64, 1_572_864, "float32"), (64, 1_572_863, "float32"),
+                                       (32, 100_000_000, "float32"), (17, 5_921_371, "float32"),
+                                       (17, 5_921_370, "float32"), (16, 100_000_000, "float32"),
+                                       (64, 1_048_576, "float32"), (64, 16_777_217, "float32"),
+                                       (20, 10_066_330, "bfloat16"), (20, 10_066_329, "bfloat16"),
+                                       (33, 4_194_304, "bfloat16")])
+def test_fused_allreduce_split_is_modelled(coll, n, t, dtype):
+    """From 17 ranks and 384 MiB of inputs the fused AllReduces are two
     launches moving (2N+1) T s bytes; below either bound one launch of 2N T s."""
     s = 2 if dtype == "bfloat16" else 4
-    alpha, gbps = ar.get_cost_model("ring_allreduce", "fused")
+    alpha, gbps = ar.get_cost_model(coll, "fused")
     split = _split(n, t, s)
-    assert split == (n >= 33 and n * t * s >= 1 << 28)
+    assert split == (n >= 17 and n * t * s >= 402_653_184)
     launches, nbytes = (2, (2 * n + 1) * t * s) if split else (1, 2 * n * t * s)
     want = launches * alpha + nbytes / (gbps * 1e3)
-    assert ar.predict_time("ring_allreduce", "fused", n, t, dtype) == pytest.approx(want, rel=1e-12)
+    assert ar.predict_time(coll, "fused", n, t, dtype) == pytest.approx(want, rel=1e-12)
 
 
 def test_allreduce_choice_switches_at_the_model_crossover():
@@ -297,16 +303,16 @@ def test_allreduce_choice_switches_at_the_model_crossover():
 
 def test_default_model_ties_the_fused_ring_and_tree():
     """The shipped coefficients give the fused ring and the fused double tree
-    one shared fit (same launches, same bytes), so every size up to 32 ranks
-    predicts a tie and the size-based choice runs the ring (above 32 ranks
-    a large fused ring is two launches); under the step implementation the
-    tree wins small messages (fewer launches) and the ring large ones."""
+    one shared fit (same launches, same bytes, split alike), so every size
+    predicts a tie and the size-based choice runs the ring; under the step
+    implementation the tree wins small messages (fewer launches) and the ring
+    large ones."""
     assert ar.get_cost_model("ring_allreduce", "fused") == ar.get_cost_model("tree_allreduce", "fused")
     old = ar.get_impl()
     try:
         ar.set_impl("fused")
         for t in (1, 256, 262_144, 4_194_304, 67_108_864, 300_000_000):
-            for n in (2, 4, 8, 32):
+            for n in (2, 4, 8, 17, 32, 64):
                 assert ar.predict_time("ring_allreduce", "fused", n, t, "float32") == \
                     ar.predict_time("tree_allreduce", "fused", n, t, "float32")
                 assert ar.allreduce_choice(n, t, "float32") == "ring_allreduce"

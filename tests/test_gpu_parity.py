@@ -507,11 +507,13 @@ def test_zero_n64_reduce_scatter_then_allgather_and_broadcast():
 
 
 def test_split_ring_allreduce_many_ranks():
-    """From 33 ranks and 256 MiB of inputs the fused ring AllReduce runs as the
+    """From 17 ranks and 384 MiB of inputs the fused ring AllReduce runs as the
     fused ReduceScatter followed by the fan-out AllGather.  N=64 x 16,777,217
     float32 (ragged chunks): sampled windows against the oracle and whole
     buffers against the step implementation (the literal schedule); N=40 x
-    16,777,259 bfloat16, per hop and with float32 partials: sampled windows."""
+    16,777,259 bfloat16, per hop and with float32 partials: sampled windows;
+    N=17 x 5,921,371 int32 MAX, the smallest split size at 17 ranks: sampled
+    windows and whole buffers against the step implementation."""
     w = workloads.WORKLOADS["zero_n64"]
     size = -(-w.count // w.nranks)
     cuts = [c * size for c in range(1, w.nranks, 9)] + [63 * size]
@@ -548,10 +550,10 @@ def test_split_ring_allreduce_many_ranks():
         assert _ranks_identical(bufs)
         del bufs, saved
         torch.cuda.empty_cache()
-    # int32 MAX at the smallest split size class: fused (two launches) on
-    # sampled windows against the oracle, and whole buffers against the
+    # int32 MAX at the smallest split size at 17 ranks: fused (two launches)
+    # on sampled windows against the oracle, and whole buffers against the
     # literal schedule
-    n, t = 33, 2_033_603
+    n, t = 17, 5_921_371
     size = -(-t // n)
 
     def draw():
@@ -564,7 +566,7 @@ def test_split_ring_allreduce_many_ranks():
         bufs = draw()
         if impl == "fused":
             check_windows("ring_allreduce", bufs, lambda b: ar.ring_allreduce(b, op="max"), "int32",
-                          op="max", cuts=[c * size for c in range(1, n, 7)], seed=23, ranks=[0, 32])
+                          op="max", cuts=[c * size for c in range(1, n, 4)], seed=23, ranks=[0, 16])
         else:
             announce(f"ring_allreduce max n={n} t={t} int32 impl=step")
             ar.ring_allreduce(bufs, op="max")
@@ -574,6 +576,77 @@ def test_split_ring_allreduce_many_ranks():
     assert all(torch.equal(x, y) for x, y in zip(*outs))
     del outs
     torch.cuda.empty_cache()
+
+
+def test_split_tree_allreduce_many_ranks():
+    """From 17 ranks and 384 MiB of inputs the fused double-tree AllReduce runs
+    as both trees' folds stored into their roots (rank 0, rank N-1), then the
+    two halves fanned out from those roots.  N=64 x 16,777,217 float32:
+    sampled windows against the oracle (cuts at the halves' boundary) and
+    whole buffers against the step implementation (the literal rounds);
+    N=17 x 5,921,371 int32 MIN, the smallest split size at 17 ranks: the same;
+    N=40 x 16,777,259 bfloat16, per hop and with float32 partials: windows."""
+    w = workloads.WORKLOADS["zero_n64"]
+    half = -(-w.count // 2)
+    cuts = [half, half - 1, half + 1, w.count // 3]
+    ar.set_impl("fused")
+    a = _device_inputs(w)
+    check_windows("tree_allreduce", a, lambda b: ar.tree_allreduce(b), w.dtype, cuts=cuts,
+                  seed=31, ranks=[0, 1, 31, 62, 63])
+    assert _ranks_identical(a)
+    ar.set_impl("step")
+    b = _device_inputs(w)
+    announce("tree_allreduce impl=step n=64 whole buffers")
+    ar.tree_allreduce(b)
+    torch.cuda.synchronize()
+    ar.set_impl("fused")
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+
+    n, t = 17, 5_921_371
+    half = -(-t // 2)
+
+    def draw():
+        return [workloads.device_rank("int_uniform", "int32", t, 33, r, DEV, {"lo": -1000, "hi": 1000})
+                for r in range(n)]
+
+    outs = []
+    for impl in ("fused", "step"):
+        ar.set_impl(impl)
+        bufs = draw()
+        if impl == "fused":
+            check_windows("tree_allreduce", bufs, lambda x: ar.tree_allreduce(x, op="min"), "int32",
+                          op="min", cuts=[half, half + 3], seed=33, ranks=[0, 8, 16])
+        else:
+            announce(f"tree_allreduce min n={n} t={t} int32 impl=step")
+            ar.tree_allreduce(bufs, op="min")
+            torch.cuda.synchronize()
+        outs.append(bufs)
+    ar.set_impl("fused")
+    assert all(torch.equal(x, y) for x, y in zip(*outs))
+    del outs
+    torch.cuda.empty_cache()
+
+    n, t = 40, 16_777_259
+    half = -(-t // 2)
+    wins = _windows(t, [half, half - 5, 1 << 20], 37)
+    for acc in (None, "float32"):
+        bufs = [workloads.device_rank("normal", "bfloat16", t, 37, r, DEV, {"std": 1e-3})
+                for r in range(n)]
+        saved = [(lo, hi, _window_host(bufs, lo, hi, "bfloat16")) for lo, hi in wins]
+        announce(f"tree_allreduce n={n} t={t} bfloat16 accumulate={acc}")
+        ar.tree_allreduce(bufs, accumulate=acc)
+        torch.cuda.synchronize()
+        odt = "bfloat16_acc32" if acc else "bfloat16"
+        for lo, hi, xin in saved:
+            want = oracle.tree_allreduce(xin, "sum", odt, window_start=lo, total=t).bufs
+            for r in (0, 19, 39):
+                assert_same(to_host(bufs[r][lo:hi], "bfloat16"), want[r], "bfloat16",
+                            f"{odt} window {lo} rank {r}")
+        assert _ranks_identical(bufs)
+        del bufs, saved
+        torch.cuda.empty_cache()
 
 
 def test_zero_n64_reduce_scatter_gather_full_size():

@@ -134,7 +134,7 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
   if (coll == AR_REDUCE) {
     // one implementation: the partials of the rounds live in registers, so
     // no rank other than the root is written
-    err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, root, vec, stream);
+    err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, root, false, vec, stream);
   } else if (coll == AR_ALLTOALL) {
     err = ar::launch_alltoall(ptrs, n, count, dtype, vec, stream);
   } else if (impl == AR_IMPL_STEP || coll == AR_SCATTER || coll == AR_GATHER) {
@@ -147,7 +147,7 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
   } else {
     switch (coll) {
       case AR_RING_ALLREDUCE:
-        if (ar::ring_allreduce_split(n, count, ar::itemsize(dtype))) {
+        if (ar::allreduce_split(n, count, ar::itemsize(dtype))) {
           // fused ReduceScatter, then the owners' chunks fanned out: the same
           // bits as the one-pass fold (AllReduce = AllGather after
           // ReduceScatter), faster for many ranks
@@ -167,7 +167,15 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
         err = ar::launch_fanout(ptrs, n, count, dtype, true, root, vec, stream);
         break;
       case AR_TREE_ALLREDUCE:
-        err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, vec, stream);
+        if (ar::allreduce_split(n, count, ar::itemsize(dtype))) {
+          // both trees' folds stored into their roots, then each root's half
+          // fanned out: the reduce and broadcast passes, the same bits as the
+          // one-pass fold, faster for many ranks
+          err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, true, vec, stream);
+          if (err == hipSuccess) err = ar::launch_tree_broadcast(ptrs, n, count, dtype, vec, stream);
+        } else {
+          err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, false, vec, stream);
+        }
         break;
       default:   // Reduce, Scatter, Gather and AllToAll are dispatched above
         break;

@@ -1,9 +1,10 @@
 // Copy kernels (gfx950).
 //
 // Fan-out: AllGather (chunk c comes from rank c, its owner after
-// ReduceScatter) or Broadcast (every chunk comes from the root).  The chunk
-// split only spreads the work over blockIdx.y; each element is read once
-// from its source rank and written into every other rank.
+// ReduceScatter), Broadcast (every chunk comes from the root) or the double
+// tree's broadcast (two chunks, the halves, from the trees' roots: rank 0 and
+// rank N-1).  Each element is read from its source rank and written into
+// every other rank.
 //
 // AllToAll: block j of rank i and block i of rank j trade places, one thread
 // per pack of the pair, so every off-diagonal element is read once and
@@ -19,11 +20,22 @@ struct FanoutArgs {
   uint64_t chunk;
   uint64_t tiles;
   int n;
-  int root;   // < 0: AllGather
+  int root;     // >= 0: Broadcast
+  int halves;   // the double tree's two halves (else AllGather)
 };
 
-template <class T, int U, bool VEC>
+// The rank chunk c is copied from.
+__device__ __forceinline__ int fanout_source(int c, int root, int halves, int n) {
+  return root >= 0 ? root : halves ? (c == 0 ? 0 : n - 1) : c;
+}
+
+// The fan-out one element per lane: the path for rank buffers aligned only to
+// the element size (16-byte aligned buffers take the grouped kernel below).
+// blockIdx.y is the chunk.
+template <class T>
 __global__ __launch_bounds__(kBlock) void fanout_kernel(FanoutArgs a) {
+  constexpr int U = 1;
+  constexpr bool VEC = false;
   constexpr int K = PackOf<T, VEC>::K;
   using P = typename PackOf<T, VEC>::P;
   using S = Pack<T, 1>;
@@ -33,7 +45,7 @@ __global__ __launch_bounds__(kBlock) void fanout_kernel(FanoutArgs a) {
   const uint64_t lo = umin(static_cast<uint64_t>(c) * a.chunk, a.count);
   const uint64_t hi = umin(lo + a.chunk, a.count);
   if (lo >= hi) return;
-  const int src = a.root < 0 ? c : a.root;
+  const int src = fanout_source(c, a.root, a.halves, n);
   const Span s = make_span<K>(lo, hi);
 
   for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
@@ -63,12 +75,135 @@ __global__ __launch_bounds__(kBlock) void fanout_kernel(FanoutArgs a) {
   }
 }
 
+// The fan-out for 16-byte packs, in destination passes.  Written as above
+// (every block storing its tile into all N-1 other ranks), the blocks in
+// flight at any moment write into every rank buffer at once.  Measured on
+// gfx950, a write stream spread that way over 63 buffers runs at about 71 %
+// of HBM peak where the same bytes written one buffer after another run at
+// 78 %, and the fan-out itself ran at 65-68 %.  So the tile slots (a.slots
+// per chunk, chunk after chunk) are cut into groups of a.group slots, and
+// each group is copied pass by pass: a pass writes every tile of the group
+// into one rank, so the blocks in flight together fill one contiguous
+// stretch of one buffer.  Every pass re-reads the group's source tiles: with
+// a.group a multiple of 8, tile q runs on the same XCD in every pass (blocks
+// go to the 8 XCDs in turn), and the group fits in the XCDs' L2, so HBM still
+// sees each source byte read once (FETCH_SIZE confirms it).  Unit b of the
+// flattened launch is (group, pass, slot).
+struct FanoutGroupArgs {
+  RankPtrs ptrs;
+  uint64_t count;
+  uint64_t chunk;
+  uint32_t slots;   // tile slots per chunk
+  uint32_t group;   // tile slots per group (a multiple of 8)
+  uint32_t units;   // groups * passes * group
+  int n;
+  int nchunks;      // n, or 2 for the double tree's halves
+  int passes;
+  int root;         // >= 0: Broadcast
+  int halves;       // the double tree's halves (else AllGather)
+  int rotate;       // pass j writes rank src + 1 + j (else rank j, or j + 1 past the root)
+};
+
+template <class T, int U, bool NTL, bool NTS>
+__global__ __launch_bounds__(kBlock) void fanout_group_kernel(FanoutGroupArgs a) {
+  constexpr int K = 16 / sizeof(T);
+  using S = Pack<T, 1>;
+  const int n = a.n;
+  const uint32_t per_group = a.group * static_cast<uint32_t>(a.passes);
+
+  // (the host keeps units + gridDim.x below 2^32)
+  for (uint32_t b = blockIdx.x; b < a.units; b += gridDim.x) {
+    // the unit's coordinates are wave-uniform; readfirstlane keeps them (and
+    // the rank pointers they select) in scalar registers
+    const uint32_t g = b / per_group;
+    const uint32_t rem = b - g * per_group;
+    const int j = wave_uniform(static_cast<int>(rem / a.group));
+    const uint32_t q = g * a.group + (rem - static_cast<uint32_t>(j) * a.group);
+    const int c = wave_uniform(static_cast<int>(q / a.slots));
+    if (c >= a.nchunks) continue;   // padding of the last group
+    const uint32_t lt = static_cast<uint32_t>(wave_uniform(static_cast<int>(q - static_cast<uint32_t>(c) * a.slots)));
+    const int src = fanout_source(c, a.root, a.halves, n);
+    const int dst = a.rotate ? wrap_rank(src + 1 + j, n) : (a.root >= 0 && j >= a.root) ? j + 1 : j;
+    if (dst == src) continue;
+    const uint64_t lo = umin(static_cast<uint64_t>(c) * a.chunk, a.count);
+    const uint64_t hi = umin(lo + a.chunk, a.count);
+    if (lo >= hi) continue;
+    const Span s = make_span<K>(lo, hi);
+
+    const uint64_t tp = TileGrid<U>::first_pack(s.plo, lt);
+    if (tp < s.phi) {
+      const uint64_t toff = tp * 16;
+      const TileLanes<U, 16> ln(tp, s.plo, s.phi);
+      // plain loads, so that the later passes find these lines in L2; with
+      // a single pass (two ranks) nothing is read twice and the loads stream
+      const char* sp = at(a.ptrs.p[src], toff);
+      char* dp = at(a.ptrs.p[dst], toff);
+      Raw16 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (ln.live[u]) {
+          const Raw16* ap = reinterpret_cast<const Raw16*>(sp + ln.off[u]);
+          v[u] = NTL ? __builtin_nontemporal_load(ap) : *ap;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (ln.live[u]) {
+          Raw16* bp = reinterpret_cast<Raw16*>(dp + ln.off[u]);
+          if (NTS)
+            __builtin_nontemporal_store(v[u], bp);
+          else
+            *bp = v[u];
+        }
+      }
+    }
+
+    // the chunk's elements outside whole packs: one unit per chunk (its first
+    // slot, in the pass of the rank after the source) copies them everywhere
+    if (lt == 0 && dst == wrap_rank(src + 1, n) && threadIdx.x < s.scalar_count()) {
+      const uint64_t e = s.scalar_index(threadIdx.x);
+      const S v = load<S>(a.ptrs.p[src], e);
+      for (int r = 0; r < n; ++r)
+        if (r != src) store<S>(a.ptrs.p[r], e, v);
+    }
+  }
+}
+
+// Bytes of source per group (before balancing): 12 MiB, 1.5 MiB of each
+// XCD's 4 MiB L2.  Measured on gfx950 against 4, 8 and 16 MiB over AllGathers
+// of 16 to 64 ranks, it was fastest or within the noise of the fastest.
+constexpr uint64_t kFanoutGroupBytes = 12ull << 20;
+
+// Loads and stores of the grouped fan-out, measured on gfx950 against each
+// other: with two ranks (one pass, nothing read twice) the copy streams its
+// loads and stores through the caches; with more, the loads go through L2
+// for the later passes and the stores stream.
+struct FanoutFlavour {
+  int unroll;
+  bool stream_loads;
+  bool stream_stores;
+};
+
+inline FanoutFlavour fanout_flavour(int n) {
+  if (n == 2) return {4, true, false};
+  return {2, false, true};
+}
+
+template <class T, int U>
+const void* fanout_group_fn(bool ntl, bool nts) {
+  if (ntl) {
+    return nts ? reinterpret_cast<const void*>(&fanout_group_kernel<T, U, true, true>)
+               : reinterpret_cast<const void*>(&fanout_group_kernel<T, U, true, false>);
+  }
+  return nts ? reinterpret_cast<const void*>(&fanout_group_kernel<T, U, false, true>)
+             : reinterpret_cast<const void*>(&fanout_group_kernel<T, U, false, false>);
+}
+
 template <class T>
-const void* fanout_fn(int u, bool vec) {
-  if (!vec) return reinterpret_cast<const void*>(&fanout_kernel<T, 1, false>);
-  if (u == 4) return reinterpret_cast<const void*>(&fanout_kernel<T, 4, true>);
-  if (u == 2) return reinterpret_cast<const void*>(&fanout_kernel<T, 2, true>);
-  return reinterpret_cast<const void*>(&fanout_kernel<T, 1, true>);
+const void* fanout_group_fn(int u, bool ntl, bool nts) {
+  if (u == 4) return fanout_group_fn<T, 4>(ntl, nts);
+  if (u == 2) return fanout_group_fn<T, 2>(ntl, nts);
+  return fanout_group_fn<T, 1>(ntl, nts);
 }
 
 // AllToAll block swap: blockIdx.y = i * n + j; pairs with i >= j exit (the
@@ -139,20 +274,78 @@ hipError_t launch_alltoall(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype
   return launch(fn, grid, a, stream);
 }
 
-hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                         bool from_root, int root, bool vec, hipStream_t stream) {
+namespace {
+
+// One fan-out launch: `nchunks` chunks of `chunk` elements, chunk c copied
+// from fanout_source(c, root, halves, n) into every other rank.
+hipError_t launch_fanout_chunks(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                                uint64_t chunk, int nchunks, int root, bool halves, bool vec,
+                                hipStream_t stream) {
+  if (vec) {
+    FanoutGroupArgs a;
+    a.ptrs = ptrs;
+    a.count = count;
+    a.chunk = chunk;
+    a.n = n;
+    a.nchunks = nchunks;
+    a.root = root;
+    a.halves = halves ? 1 : 0;
+    const FanoutFlavour fl = fanout_flavour(n);
+    const int u = pick_fanout_unroll(fl.unroll);
+    const int pack = static_cast<int>(16 / itemsize(dtype));
+    const uint64_t slots = tiles_for(chunk, pack, u);
+    const uint64_t tile_bytes = static_cast<uint64_t>(kBlock) * u * 16;
+    const uint64_t all_slots = slots * static_cast<uint64_t>(nchunks);
+    // groups of about kFanoutGroupBytes, balanced so that the last one is
+    // not mostly padding
+    const uint64_t group_max = std::max<uint64_t>(8, kFanoutGroupBytes / tile_bytes / 8 * 8);
+    const uint64_t groups = (all_slots + group_max - 1) / group_max;
+    const uint64_t group = ((all_slots + groups - 1) / groups + 7) / 8 * 8;
+    // A group inside one or two chunks has one source per tile, so pass j can
+    // write rank src + 1 + j: n - 1 passes, each one buffer.  A group over
+    // many small chunks keeps one destination per pass instead (pass j
+    // writes rank j, or j + 1 past a Broadcast's root; the tiles whose source
+    // is rank j have nothing to do).
+    a.rotate = (root >= 0 || slots * 2 >= group) ? 1 : 0;
+    a.passes = (a.rotate || root >= 0) ? n - 1 : n;
+    const uint64_t units = (all_slots + group - 1) / group * group * static_cast<uint64_t>(a.passes);
+    // the decode runs in 32 bits; all rank buffers together would have to
+    // exceed the GPU's memory many times over to need more (the element
+    // path below takes such a call)
+    if (units + kMaxGridX <= UINT32_MAX) {
+      a.slots = static_cast<uint32_t>(slots);
+      a.group = static_cast<uint32_t>(group);
+      a.units = static_cast<uint32_t>(units);
+      const void* fn = itemsize(dtype) == 2 ? fanout_group_fn<uint16_t>(u, fl.stream_loads, fl.stream_stores)
+                                            : fanout_group_fn<uint32_t>(u, fl.stream_loads, fl.stream_stores);
+      return launch(fn, dim3(grid_x(units)), a, stream);
+    }
+  }
   FanoutArgs a;
   a.ptrs = ptrs;
   a.count = count;
-  a.chunk = chunk_size(n, count);
+  a.chunk = chunk;
   a.n = n;
-  a.root = from_root ? root : -1;
-  const int pack = vec ? static_cast<int>(16 / itemsize(dtype)) : 1;
-  const int u = vec ? pick_fanout_unroll(n) : 1;
-  a.tiles = tiles_for(a.chunk, pack, u);
-  const dim3 grid(grid_x(a.tiles), n);
-  const void* fn = itemsize(dtype) == 2 ? fanout_fn<uint16_t>(u, vec) : fanout_fn<uint32_t>(u, vec);
+  a.root = root;
+  a.halves = halves ? 1 : 0;
+  a.tiles = tiles_for(chunk, 1, 1);
+  const dim3 grid(grid_x(a.tiles), static_cast<uint32_t>(nchunks));
+  const void* fn = itemsize(dtype) == 2 ? reinterpret_cast<const void*>(&fanout_kernel<uint16_t>)
+                                        : reinterpret_cast<const void*>(&fanout_kernel<uint32_t>);
   return launch(fn, grid, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                         bool from_root, int root, bool vec, hipStream_t stream) {
+  return launch_fanout_chunks(ptrs, n, count, dtype, chunk_size(n, count), n, from_root ? root : -1,
+                              false, vec, stream);
+}
+
+hipError_t launch_tree_broadcast(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                                 bool vec, hipStream_t stream) {
+  return launch_fanout_chunks(ptrs, n, count, dtype, tree_split(count), 2, -1, true, vec, stream);
 }
 
 }  // namespace ar

@@ -477,21 +477,18 @@ inline uint64_t tiles_for(uint64_t max_elems, int pack, int unroll) {
   return (packs + per_tile - 1) / per_tile + 1;
 }
 
-// Packs per lane per tile of the fan-out copy.  Measured on gfx950 by
-// alternating both choices in one process over about 10 GB of rank buffers:
-// four packs are best for N <= 8 and two above (one pack is 11 % slower at
-// N = 64).  AR_TUNE_UNROLL (1, 2 or 4), read at the first launch, overrides
-// the choice for measurements; it changes nothing but the pack grouping,
-// never any element's arithmetic.  (The folds stage their tiles through LDS
-// and have no such choice.)
-inline int pick_fanout_unroll(int n) {
+// Packs per lane per tile of the fan-out copy: `preferred` unless
+// AR_TUNE_UNROLL (1, 2 or 4, read at the first launch) overrides it for
+// measurements; the choice changes nothing but the pack grouping, never any
+// element's arithmetic.  (The folds stage their tiles through LDS and have
+// no such choice.)
+inline int pick_fanout_unroll(int preferred) {
   static const int forced = [] {
     const char* v = std::getenv("AR_TUNE_UNROLL");
     const int u = v != nullptr ? std::atoi(v) : 0;
     return (u == 1 || u == 2 || u == 4) ? u : 0;
   }();
-  if (forced != 0) return forced;
-  return n <= 8 ? 4 : 2;
+  return forced != 0 ? forced : preferred;
 }
 
 inline uint32_t grid_x(uint64_t tiles) {

@@ -30,17 +30,24 @@ hipError_t launch_ring_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtyp
 hipError_t launch_fanout(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
                          bool from_root, int root, bool vec, hipStream_t stream);
 
+// The double tree's broadcast as one fan-out: elements [0, ceil(T/2)) copied
+// from rank 0 (tree 0's root), [ceil(T/2), T) from rank N-1 (tree 1's root),
+// into every other rank.
+hipError_t launch_tree_broadcast(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
+                                 bool vec, hipStream_t stream);
+
 // AllToAll: block j of rank i and block i of rank j swap places for every
 // pair i < j (count must be a multiple of n).
 hipError_t launch_alltoall(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype, bool vec,
                            hipStream_t stream);
 
 // Fused binomial tree fold.  root < 0: the double tree, per element the
-// pairwise fold of the tree that owns it, stored into every rank.  root >= 0:
-// Reduce, one tree over the whole buffer on roles (rank - root) mod N, stored
-// into bufs[root] only.
+// pairwise fold of the tree that owns it, stored into every rank (or, with
+// to_roots, into the owning tree's root only: rank 0 for [0, ceil(T/2)),
+// rank N-1 for the rest).  root >= 0: Reduce, one tree over the whole buffer
+// on roles (rank - root) mod N, stored into bufs[root] only.
 hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                            ar_op_t op, int root, bool vec, hipStream_t stream);
+                            ar_op_t op, int root, bool to_roots, bool vec, hipStream_t stream);
 
 // One schedule step: all of its transfers in one launch.
 hipError_t launch_step(const RankPtrs& ptrs, const Step& step, ar_dtype_t dtype, ar_op_t op,

@@ -291,15 +291,16 @@ int expected_steps(ar_collective_t coll, int n) {
   return -1;
 }
 
-bool ring_allreduce_split(int n, uint64_t count, size_t isz) {
-  constexpr int kMinRanks = 33;
-  constexpr uint64_t kMinInputBytes = 1ull << 28;
+bool allreduce_split(int n, uint64_t count, size_t isz) {
+  constexpr int kMinRanks = 17;
+  constexpr uint64_t kMinInputBytes = 3ull << 27;   // 384 MiB
   return n >= kMinRanks && static_cast<uint64_t>(n) * count * isz >= kMinInputBytes;
 }
 
 int impl_launches(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz) {
   if (n <= 1) return 0;
-  if (impl == AR_IMPL_FUSED && coll == AR_RING_ALLREDUCE && ring_allreduce_split(n, count, isz))
+  if (impl == AR_IMPL_FUSED && (coll == AR_RING_ALLREDUCE || coll == AR_TREE_ALLREDUCE) &&
+      allreduce_split(n, count, isz))
     return 2;
   // Reduce has one (fused) implementation; Scatter, Gather and AllToAll are
   // one step.
@@ -317,8 +318,8 @@ uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t co
   if (fused && coll != AR_SCATTER && coll != AR_GATHER && coll != AR_ALLTOALL) {
     switch (coll) {
       case AR_RING_ALLREDUCE:
-        return (ring_allreduce_split(n, count, isz) ? 2 * un + 1 : 2 * un) * count * isz;
-      case AR_TREE_ALLREDUCE: return 2 * un * count * isz;
+      case AR_TREE_ALLREDUCE:
+        return (allreduce_split(n, count, isz) ? 2 * un + 1 : 2 * un) * count * isz;
       case AR_REDUCE_SCATTER:
       case AR_REDUCE: return (un + 1) * count * isz;
       default: return un * count * isz;   // AllGather, Broadcast

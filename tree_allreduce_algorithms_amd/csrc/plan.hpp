@@ -69,25 +69,29 @@ int expected_steps(ar_collective_t coll, int n);
 // launches once per schedule step and moves 3 bytes per element of each
 // reduce transfer (read both sides, write one) and 2 per element of each copy
 // transfer.
-// The fused ring AllReduce of many ranks runs as two launches (see
-// ring_allreduce_split), moving (2N + 1) * T * s bytes.
+// The fused AllReduces of many ranks run as two launches (see
+// allreduce_split), moving (2N + 1) * T * s bytes.
 int impl_launches(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz);
 uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t count, size_t isz);
 
-// Whether the fused ring AllReduce runs as the fused ReduceScatter (every
-// element folded in ring order into its owner's chunk) followed by the fused
-// AllGather (each owner's chunk copied to every other rank) instead of one
-// fold that stores into all N ranks.  Both give the same bits: AllReduce is
-// AllGather after ReduceScatter [Lecture 09 section 3.9], and the
-// ReduceScatter leaves exactly the value the one-pass fold stores.  Measured
-// on gfx950 (in-process A/B, float32, both folds through LDS-staged tiles),
-// the two phases win above 32 ranks although they move T * s more bytes: the
-// one-pass fold's stores to every rank become deep per-wave store bursts
-// there.  With 9.6 GB of inputs: N = 33 +1 %, 40 +2 %, 48 +3 %, 64 +5 %; with
-// 512 MiB (N = 64) +19 %.  At 32 ranks and 9.6 GB the one-pass fold is 5-8 %
-// faster, so the split starts at 33 ranks; below 256 MiB of inputs (Infinity
-// Cache resident) one launch stays.
-bool ring_allreduce_split(int n, uint64_t count, size_t isz);
+// Whether the fused AllReduces run in two launches instead of one fold that
+// stores into all N ranks: the ring as the fused ReduceScatter (every
+// element folded in ring order into its owner's chunk) then the fused
+// AllGather (each owner's chunk copied to every other rank); the double tree
+// as its two trees' folds stored into their roots only (rank 0 and rank N-1)
+// then each root's half copied to every other rank.  Both give the same bits
+// as the one-pass folds: AllReduce is AllGather after ReduceScatter [Lecture
+// 09 section 3.9], a tree AllReduce is its reduce then its broadcast [Lecture
+// 09 section 5.2], and the first launch leaves exactly the value the one-pass
+// fold stores.  With many ranks the one-pass fold writes every tile into all
+// N buffers at once, which HBM serves poorly, while the copy writes one
+// buffer after another.  Measured on gfx950 (in-process A/B, float32, 17 to
+// 64 ranks): with 384 MiB to 4.8 GB of inputs the two launches are 1-13 %
+// faster than the one-pass fold for both algorithms, except the ring at 24
+// ranks and 805 MB (even); with exactly 256 MiB (the Infinity Cache's size)
+// they are 1-7 % slower for most rank counts; at 12 and 16 ranks (1.2 GB)
+// the one-pass folds tie.  So both split from 17 ranks and 384 MiB of inputs.
+bool allreduce_split(int n, uint64_t count, size_t isz);
 
 // Validation shared by every collective call.  `op` < 0 means "not used",
 // `root` < 0 means "not used".  Checks: bufs non-NULL, n in range, dtype /

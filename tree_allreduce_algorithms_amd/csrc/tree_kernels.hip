@@ -29,7 +29,8 @@ struct TreeArgs {
   uint64_t half;
   uint64_t tiles;
   int n;
-  int root;   // >= 0: Reduce to `root` (one tree over the whole buffer)
+  int root;       // >= 0: Reduce to `root` (one tree over the whole buffer)
+  int to_roots;   // double tree: store each tree's result into its root only
 };
 
 constexpr int kTreeBatch = 8;
@@ -41,6 +42,22 @@ constexpr int ilog2_ceil(int v) { return v <= 1 ? 0 : 1 + ilog2_ceil((v + 1) / 2
 __device__ __forceinline__ int tree_role_rank(int role, int tree, int root, int n) {
   return root >= 0 ? wrap_rank(role + root, n) : (tree == 0 ? role : n - 1 - role);
 }
+
+// The ranks [lo, hi) that receive tree `tree`'s result: the root of a Reduce,
+// the tree's own root (role 0) when the double tree stores into its roots
+// only, every rank otherwise.
+struct OutRanks {
+  int lo, hi;
+  __device__ OutRanks(const TreeArgs& a, int tree) {
+    if (a.root >= 0 || a.to_roots) {
+      lo = tree_role_rank(0, tree, a.root, a.n);
+      hi = lo + 1;
+    } else {
+      lo = 0;
+      hi = a.n;
+    }
+  }
+};
 
 // The binary counter over roles 0, 1, ..., N-1 described above, for U values
 // per role.  push() takes the roles in order; its role must be a compile-time
@@ -151,7 +168,8 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
           return ln.live[u] ? load_stream<P>(at(a.ptrs.p[rank], toff), ln.off[u]) : P{};
         },
         v);
-    for (int r = root >= 0 ? root : 0; r < (root >= 0 ? root + 1 : n); ++r) {
+    const OutRanks out(a, tree);
+    for (int r = out.lo; r < out.hi; ++r) {
       char* dst = at(a.ptrs.p[r], toff);
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -164,8 +182,8 @@ __global__ __launch_bounds__(kBlock) void tree_fold_kernel(TreeArgs a) {
     S v[1];
     tree_fold_values<DT, OP, NMAX, 1, S>(
         n, tree, root, [&](int rank, int) { return load<S>(a.ptrs.p[rank], e); }, v);
-    for (int r = root >= 0 ? root : 0; r < (root >= 0 ? root + 1 : n); ++r)
-      store<S>(a.ptrs.p[r], e, v[0]);
+    const OutRanks out(a, tree);
+    for (int r = out.lo; r < out.hi; ++r) store<S>(a.ptrs.p[r], e, v[0]);
   }
 }
 
@@ -179,7 +197,8 @@ struct TreeSlot {
 // M runs of 64 packs of each role in LDS, a group of kStageGroup roles at a
 // time (roles 0-31, then 32-63), each thread pushes whole 32-bit words of the
 // tile's columns through the counter above in role order, and the results go
-// to every rank (double tree) or to the root (Reduce).
+// to every rank (double tree), to the tree's root (double tree, to_roots) or
+// to the root (Reduce).
 template <ar_dtype_t DT, ar_op_t OP, int NMAX>
 __global__ __launch_bounds__(kBlock) void tree_stage_kernel(TreeArgs a) {
   using T = typename Elem<DT>::T;
@@ -235,10 +254,12 @@ __global__ __launch_bounds__(kBlock) void tree_stage_kernel(TreeArgs a) {
     }
     // (the next tile's first barrier orders these reads of res before its
     // fold overwrites them)
-    if (root >= 0)
-      stage_out<1, M>(a.ptrs, root, root + 1, t, res);
-    else
+    if (root >= 0 || a.to_roots) {
+      const int r = tree_role_rank(0, tree, root, n);
+      stage_out<1, M>(a.ptrs, r, r + 1, t, res);
+    } else {
       stage_out<NMAX, M>(a.ptrs, 0, n, t, res);
+    }
   }
 
   if (blockIdx.x == 0 && threadIdx.x < s.scalar_count()) {
@@ -246,8 +267,8 @@ __global__ __launch_bounds__(kBlock) void tree_stage_kernel(TreeArgs a) {
     S v[1];
     tree_fold_values<DT, OP, NMAX, 1, S>(
         n, tree, root, [&](int rank, int) { return load<S>(a.ptrs.p[rank], e); }, v);
-    for (int r = root >= 0 ? root : 0; r < (root >= 0 ? root + 1 : n); ++r)
-      store<S>(a.ptrs.p[r], e, v[0]);
+    const OutRanks out(a, tree);
+    for (int r = out.lo; r < out.hi; ++r) store<S>(a.ptrs.p[r], e, v[0]);
   }
 }
 
@@ -289,7 +310,7 @@ hipError_t tree_fold_typed(const TreeArgs& a, bool vec, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype_t dtype,
-                            ar_op_t op, int root, bool vec, hipStream_t stream) {
+                            ar_op_t op, int root, bool to_roots, bool vec, hipStream_t stream) {
   TreeArgs a;
   a.ptrs = ptrs;
   a.count = count;
@@ -297,6 +318,7 @@ hipError_t launch_tree_fold(const RankPtrs& ptrs, int n, uint64_t count, ar_dtyp
   a.n = n;
   a.tiles = 0;
   a.root = root;
+  a.to_roots = (root < 0 && to_roots) ? 1 : 0;
   AR_DISPATCH_FOLD(tree_fold_typed, dtype, op, a, vec, stream);
 }
 
