@@ -63,9 +63,13 @@ DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
 MAX_CALLS = 35
 COLLECTIVES = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce",
                "allreduce", "reduce", "scatter", "gather", "alltoall"]
-def kernel_name(collective, impl, n):
+def kernel_name(collective, impl, n, launches=1):
     """The kernel that dominates one call (16-byte aligned rank buffers): the
-    folds run through LDS-staged tiles for every N >= 2."""
+    folds run through LDS-staged tiles for every N >= 2; a fused AllReduce of
+    two launches is its fold then the fan-out."""
+    if collective in ("ring_allreduce", "tree_allreduce") and impl == "fused" and launches == 2:
+        fold = "ring_stage_kernel" if collective == "ring_allreduce" else "tree_stage_kernel"
+        return fold + " + fanout_group_kernel"
     if collective in ("ring_allreduce", "reduce_scatter") and impl == "fused":
         return "ring_stage_kernel"
     if collective == "tree_allreduce" and impl == "fused" or collective == "reduce":
@@ -397,10 +401,15 @@ def run_one(args):
     # reductions run fused under either implementation
     fused = (args.impl == "fused" or ran in ("reduce", "alltoall")
              or (acc is not None and ran in ("ring_allreduce", "reduce_scatter", "tree_allreduce")))
-    launches = 1 if fused else ar.expected_steps(ran, n)
-    moved = alg if fused else step_bytes(ran, n, t, isz, args.root)
+    # what the library runs: its launches, and for the two-launch AllReduces
+    # of many ranks the (2N+1) T s bytes they move
+    launches, impl_bytes = ar.launch_plan(ran, args.impl, n, t, odt)
+    if fused:
+        moved = impl_bytes if launches > 1 else alg
+    else:
+        moved = step_bytes(ran, n, t, isz, args.root)
     achieved = moved / (launch_ms * 1e-3) / 1e9
-    kernel = kernel_name(ran, args.impl, n)
+    kernel = kernel_name(ran, "fused" if fused else args.impl, n, launches)
     traffic = traffic_from_profile(w.name, args.collective, args.impl, per_call=launches > 1,
                                    accumulate=acc, kernel=None if launches > 1 else kernel)
 
@@ -546,6 +555,8 @@ SUITE = [
     ("zero_n64", "reduce", "fused", []),
     ("zero_n64", "scatter", "fused", []),
     ("zero_n64", "gather", "fused", []),
+    ("zero_n64", "ring_allreduce", "fused", []),
+    ("zero_n64", "tree_allreduce", "fused", []),
     ("large_grad_fp32", "reduce", "fused", []),
     ("moe_alltoall", "alltoall", "fused", []),
     ("small_int32", "ring_allreduce", "fused", ["--steps", "30"]),

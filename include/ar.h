@@ -237,13 +237,24 @@ ar_status_t ar_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t
 ar_status_t ar_allreduce_choice(int nranks, size_t count, ar_dtype_t dtype,
                                 ar_collective_t* choice);
 
+/* Kernel launches and HBM bytes of one call of `coll` under `impl` with these
+ * arguments, as the library will run it: AR_IMPL_FUSED is one launch moving
+ * every input once and every output once (2 N T s for an AllReduce), except
+ * the AllReduces from 17 ranks and 384 MiB of inputs, which are two launches
+ * moving (2 N + 1) T s; AR_IMPL_STEP is one launch per schedule step moving
+ * 3 bytes per element of every reduce transfer (read both sides, write one)
+ * and 2 per element of every copy transfer.  Reduce and AllToAll run their
+ * one kernel, Scatter and Gather their one step (root 0), under either;
+ * bfloat16 with float32 partials runs its reductions fused.  0 launches and
+ * 0 bytes when nranks == 1.  AR_ERROR_INVALID_ARGUMENT for an out-of-range
+ * argument or a NULL output pointer.  Host only. */
+ar_status_t ar_launch_plan(ar_collective_t coll, ar_impl_t impl, int nranks, size_t count,
+                           ar_dtype_t dtype, int* launches, uint64_t* hbm_bytes);
+
 /* Cost model, the single-GPU form of the pages' alpha-beta model [L09 1.3,
  * 7.3]: predicted microseconds of one call
  *     = launches * alpha_us + hbm_bytes / (gbps * 1e3)
- * where launches is 1 for AR_IMPL_FUSED and the schedule's step count for
- * AR_IMPL_STEP, and hbm_bytes is what that implementation moves (fused:
- * 2 N T s for an AllReduce; step: 3 bytes per element of every reduce
- * transfer and 2 per element of every copy transfer).  One (alpha_us, gbps)
+ * with launches and hbm_bytes those of ar_launch_plan.  One (alpha_us, gbps)
  * pair is kept per (collective, implementation); the defaults are fitted to
  * the message-size sweep measured on MI355X.  Host only. */
 ar_status_t ar_predict_time(ar_collective_t coll, ar_impl_t impl, int nranks, size_t count,

@@ -249,6 +249,53 @@ def test_predicted_time_is_the_documented_formula(coll, impl, n, t, dtype):
     assert ar.predict_time(coll, impl, n, t, dtype) == pytest.approx(want, rel=1e-12)
 
 
+@pytest.mark.parametrize("coll", sorted(ORACLE_CALLS))
+@pytest.mark.parametrize("impl", ["fused", "step"])
+@pytest.mark.parametrize("n,t,dtype", [(4, 256, "float32"), (8, 100_003, "bfloat16"),
+                                       (64, 1_000_003, "float32"), (2, 7, "int32"),
+                                       (17, 5_921_371, "float32"), (40, 16_777_259, "bfloat16"),
+                                       (1, 1000, "float32")])
+def test_launch_plan_is_the_documented_rule(coll, impl, n, t, dtype):
+    """ar_launch_plan: one launch moving the algorithmic bytes for the fused
+    kernels (two launches and (2N+1) T s for the split AllReduces), one launch
+    per schedule step for the literal schedules, the oracle's step bytes;
+    nothing for one rank."""
+    s = 2 if dtype == "bfloat16" else 4
+    launches, nbytes = ar.launch_plan(coll, impl, n, t, dtype)
+    if n == 1:
+        assert (launches, nbytes) == (0, 0)
+        return
+    if impl == "fused" or coll in ("reduce", "alltoall"):
+        want = 1
+    else:
+        want = ar.expected_steps(coll, n)
+    if impl == "fused" and coll in ("ring_allreduce", "tree_allreduce") and _split(n, t, s):
+        want = 2
+    assert launches == want
+    assert nbytes == _oracle_hbm_bytes(coll, impl, n, t, dtype)
+
+
+def test_launch_plan_float32_partials_run_fused():
+    """bfloat16 with float32 partials runs its reductions fused under either
+    setting, so the step setting plans the fused kernel for them."""
+    n, t = 8, 1_000_000
+    for coll in ("ring_allreduce", "reduce_scatter", "tree_allreduce"):
+        assert ar.launch_plan(coll, "step", n, t, "bfloat16_acc32") == \
+            ar.launch_plan(coll, "fused", n, t, "bfloat16_acc32") == (1, ar.launch_plan(coll, "fused", n, t, "bfloat16")[1])
+    assert ar.launch_plan("allgather", "step", n, t, "bfloat16_acc32")[0] == n - 1
+
+
+def test_launch_plan_arguments_are_validated():
+    lib = ar.lib()
+    n, b = ctypes.c_int(), ctypes.c_uint64()
+    assert lib.ar_launch_plan(9, 0, 4, 10, 1, ctypes.byref(n), ctypes.byref(b)) == binding.INVALID_ARGUMENT
+    assert lib.ar_launch_plan(0, 2, 4, 10, 1, ctypes.byref(n), ctypes.byref(b)) == binding.INVALID_ARGUMENT
+    assert lib.ar_launch_plan(0, 0, 65, 10, 1, ctypes.byref(n), ctypes.byref(b)) == binding.INVALID_ARGUMENT
+    assert lib.ar_launch_plan(0, 0, 4, 10, 9, ctypes.byref(n), ctypes.byref(b)) == binding.INVALID_ARGUMENT
+    assert lib.ar_launch_plan(0, 0, 4, 10, 1, None, ctypes.byref(b)) == binding.INVALID_ARGUMENT
+    assert lib.ar_launch_plan(0, 0, 4, 10, 1, ctypes.byref(n), None) == binding.INVALID_ARGUMENT
+
+
 @pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce"])
 @pytest.mark.parametrize("n,t,dtype", [(64, 1_572_864, "float32"), (64, 1_572_863, "float32"),
                                        (32, 100_000_000, "float32"), (17, 5_921_371, "float32"),

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     get_cost_model,
     get_impl,
     lib,
+    launch_plan,
     predict_time,
     raw_call,
     reduce,

@@ -36,6 +36,7 @@ SIGNATURES = {
     "ar_alltoall": (_I, [_PP, _I, _SZ, _I, _VP]),
     "ar_allreduce": (_I, [_PP, _I, _SZ, _I, _I, _VP]),
     "ar_allreduce_choice": (_I, [_I, _SZ, _I, ctypes.POINTER(_I)]),
+    "ar_launch_plan": (_I, [_I, _I, _I, _SZ, _I, ctypes.POINTER(_I), _U64P]),
     "ar_predict_time": (_I, [_I, _I, _I, _SZ, _I, ctypes.POINTER(ctypes.c_double)]),
     "ar_set_cost_model": (_I, [_I, _I, ctypes.c_double, ctypes.c_double]),
     "ar_get_cost_model": (_I, [_I, _I, ctypes.POINTER(ctypes.c_double),
@@ -342,6 +343,14 @@ def allreduce_choice(nranks, count, dtype):
     _check(lib().ar_allreduce_choice(nranks, count, DTYPES[dtype], ctypes.byref(out)),
            "allreduce_choice")
     return {v: k for k, v in COLLECTIVES.items()}[out.value]
+
+
+def launch_plan(collective, impl, nranks, count, dtype):
+    """(kernel launches, HBM bytes) of one call as the library runs it."""
+    n, b = ctypes.c_int(), ctypes.c_uint64()
+    _check(lib().ar_launch_plan(COLLECTIVES[collective], IMPLS[impl], nranks, count,
+                                DTYPES[dtype], ctypes.byref(n), ctypes.byref(b)), "launch_plan")
+    return n.value, b.value
 
 
 def predict_time(collective, impl, nranks, count, dtype):

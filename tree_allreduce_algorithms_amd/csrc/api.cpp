@@ -49,24 +49,31 @@ struct CostCoeff {
 };
 std::mutex g_cost_mu;
 CostCoeff g_cost[9][2] = {
-    {{6.89, 6417.0}, {3.48, 6684.0}},   // ring AllReduce: fused, step
-    {{6.89, 5971.0}, {3.48, 6551.0}},   // ReduceScatter
-    {{6.89, 5400.0}, {3.48, 7450.0}},   // AllGather
-    {{6.89, 5416.0}, {3.48, 5839.0}},   // Broadcast
-    {{6.89, 6417.0}, {3.23, 5996.0}},   // double-tree AllReduce
-    {{6.89, 5651.0}, {6.89, 5651.0}},   // Reduce (fused either way)
-    {{3.48, 5058.0}, {3.48, 5058.0}},   // Scatter (one step either way)
-    {{3.48, 4982.0}, {3.48, 4982.0}},   // Gather (one step either way)
-    {{3.48, 5866.0}, {3.48, 5866.0}},   // AllToAll (one kernel either way)
+    {{7.35, 6570.0}, {3.43, 6665.0}},   // ring AllReduce: fused, step
+    {{7.35, 6477.0}, {3.43, 6649.0}},   // ReduceScatter
+    {{7.35, 5937.0}, {3.43, 7446.0}},   // AllGather
+    {{7.35, 5993.0}, {3.43, 5876.0}},   // Broadcast
+    {{7.35, 6570.0}, {3.16, 6088.0}},   // double-tree AllReduce
+    {{7.35, 6534.0}, {7.35, 6534.0}},   // Reduce (fused either way)
+    {{3.43, 5558.0}, {3.43, 5558.0}},   // Scatter (one step either way)
+    {{3.43, 5249.0}, {3.43, 5249.0}},   // Gather (one step either way)
+    {{3.43, 5904.0}, {3.43, 5904.0}},   // AllToAll (one kernel either way)
 };
 
 bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_ALLTOALL; }
 bool impl_ok(int impl) { return impl == AR_IMPL_FUSED || impl == AR_IMPL_STEP; }
 
-double predict_us(ar_collective_t coll, ar_impl_t impl, int n, size_t count, ar_dtype_t dtype) {
+// The implementation a call runs: bfloat16 with float32 partials runs its
+// reductions fused whatever the setting.
+ar_impl_t effective_impl(ar_collective_t coll, ar_impl_t impl, ar_dtype_t dtype) {
   if (dtype == AR_BFLOAT16_ACC32 &&
       (coll == AR_RING_ALLREDUCE || coll == AR_REDUCE_SCATTER || coll == AR_TREE_ALLREDUCE))
-    impl = AR_IMPL_FUSED;   // these reductions run fused for this dtype
+    return AR_IMPL_FUSED;
+  return impl;
+}
+
+double predict_us(ar_collective_t coll, ar_impl_t impl, int n, size_t count, ar_dtype_t dtype) {
+  impl = effective_impl(coll, impl, dtype);
   CostCoeff c;
   {
     std::lock_guard<std::mutex> lock(g_cost_mu);
@@ -270,6 +277,18 @@ ar_status_t ar_predict_time(ar_collective_t coll, ar_impl_t impl, int nranks, si
       !ar::dtype_ok(static_cast<int>(dtype)) || microseconds == nullptr)
     return AR_ERROR_INVALID_ARGUMENT;
   *microseconds = predict_us(coll, impl, nranks, count, dtype);
+  return AR_SUCCESS;
+}
+
+ar_status_t ar_launch_plan(ar_collective_t coll, ar_impl_t impl, int nranks, size_t count,
+                           ar_dtype_t dtype, int* launches, uint64_t* hbm_bytes) {
+  if (!coll_ok(coll) || !impl_ok(impl) || nranks < 1 || nranks > AR_MAX_RANKS ||
+      !ar::dtype_ok(static_cast<int>(dtype)) || launches == nullptr || hbm_bytes == nullptr)
+    return AR_ERROR_INVALID_ARGUMENT;
+  const ar_impl_t run = effective_impl(coll, impl, dtype);
+  const size_t isz = ar::itemsize(dtype);
+  *launches = ar::impl_launches(coll, run, nranks, count, isz);
+  *hbm_bytes = ar::impl_hbm_bytes(coll, run, nranks, count, isz);
   return AR_SUCCESS;
 }
 
