@@ -349,10 +349,6 @@ def run_one(args):
 
     stream = torch.cuda.current_stream(dev)
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_mall else None
-
-    for _ in range(args.warmup):
-        call(bufs)
-    torch.cuda.synchronize()
     # Events bracket every call when the Infinity Cache is flushed between
     # calls (the flush must stay outside them) or when a call moves enough
     # bytes that recording two events (a few microseconds of host time each)
@@ -365,11 +361,27 @@ def run_one(args):
     nev = args.steps if per_call_events else 1
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    # a reduction multiplies the values' magnitude by up to N per call: with
+    # more calls than MAX_CALLS in all, the inputs are put back after the
+    # warm-up (a device copy, so the GPU stays busy)
+    restore = (args.warmup + args.steps > MAX_CALLS
+               and args.collective in ("ring_allreduce", "tree_allreduce", "allreduce",
+                                       "reduce_scatter", "reduce"))
+    saved = [b.clone() for b in bufs] if restore else None
 
     # collect garbage now (earlier runs free large host arrays) and keep the
-    # collector out of the timed loop, which small workloads make host-bound
+    # collector out of the timed loop, which small workloads make host-bound;
+    # done before the warm-up, so that the timed calls follow it without the
+    # GPU falling idle (after an idle pause the GPU's clocks take some tens of
+    # milliseconds of load to settle, which short calls would otherwise time)
     gc.collect()
     gc.disable()
+    for _ in range(args.warmup):
+        call(bufs)
+    if saved is not None:
+        for b, v in zip(bufs, saved):
+            b.copy_(v)
+        del saved
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if per_call_events:
@@ -536,37 +548,40 @@ def run_one(args):
     return result
 
 
+# Warm-up calls per row: enough for about 20-30 ms of load before the timed
+# calls, so that they run at the GPU's settled clocks (short calls after an
+# idle pause measured up to 25 % slower for the first 10-20 calls).
 SUITE = [
     # workload, collective, impl, extra flags
     ("large_grad_fp32", "ring_allreduce", "step", []),
-    ("large_grad_fp32", "tree_allreduce", "fused", []),
-    ("large_grad_bf16", "ring_allreduce", "fused", []),
-    ("large_grad_bf16", "ring_allreduce", "step", []),
-    ("large_grad_bf16", "ring_allreduce", "fused", ["--accumulate", "float32"]),
-    ("ddp_bucket", "ring_allreduce", "fused", []),
-    ("ddp_bucket", "ring_allreduce", "fused", ["--flush-mall"]),
-    ("ddp_bucket", "ring_allreduce", "step", ["--flush-mall"]),
-    ("zero_n64", "reduce_scatter", "fused", []),
-    ("zero_n64", "allgather", "fused", []),
-    ("zero_n64", "broadcast", "fused", []),
-    ("zero_n64", "reduce_scatter", "step", []),
-    ("zero_n64", "allgather", "step", []),
-    ("zero_n64", "broadcast", "step", []),
-    ("zero_n64", "reduce", "fused", []),
-    ("zero_n64", "scatter", "fused", []),
-    ("zero_n64", "gather", "fused", []),
-    ("zero_n64", "ring_allreduce", "fused", []),
-    ("zero_n64", "tree_allreduce", "fused", []),
-    ("large_grad_fp32", "reduce", "fused", []),
-    ("moe_alltoall", "alltoall", "fused", []),
-    ("small_int32", "ring_allreduce", "fused", ["--steps", "30"]),
-    ("small_int32", "reduce_scatter", "fused", ["--steps", "30"]),
-    ("small_int32", "allgather", "fused", ["--steps", "30"]),
-    ("small_int32", "ring_allreduce", "step", ["--steps", "30"]),
+    ("large_grad_fp32", "tree_allreduce", "fused", ["--warmup", "8"]),
+    ("large_grad_bf16", "ring_allreduce", "fused", ["--warmup", "15"]),
+    ("large_grad_bf16", "ring_allreduce", "step", ["--warmup", "8"]),
+    ("large_grad_bf16", "ring_allreduce", "fused", ["--accumulate", "float32", "--warmup", "15"]),
+    ("ddp_bucket", "ring_allreduce", "fused", ["--warmup", "300"]),
+    ("ddp_bucket", "ring_allreduce", "fused", ["--flush-mall", "--warmup", "30"]),
+    ("ddp_bucket", "ring_allreduce", "step", ["--flush-mall", "--warmup", "30"]),
+    ("zero_n64", "reduce_scatter", "fused", ["--warmup", "40"]),
+    ("zero_n64", "allgather", "fused", ["--warmup", "40"]),
+    ("zero_n64", "broadcast", "fused", ["--warmup", "40"]),
+    ("zero_n64", "reduce_scatter", "step", ["--warmup", "15"]),
+    ("zero_n64", "allgather", "step", ["--warmup", "20"]),
+    ("zero_n64", "broadcast", "step", ["--warmup", "20"]),
+    ("zero_n64", "reduce", "fused", ["--warmup", "40"]),
+    ("zero_n64", "scatter", "fused", ["--warmup", "600"]),
+    ("zero_n64", "gather", "fused", ["--warmup", "600"]),
+    ("zero_n64", "ring_allreduce", "fused", ["--warmup", "20"]),
+    ("zero_n64", "tree_allreduce", "fused", ["--warmup", "20"]),
+    ("large_grad_fp32", "reduce", "fused", ["--warmup", "15"]),
+    ("moe_alltoall", "alltoall", "fused", ["--warmup", "80"]),
+    ("small_int32", "ring_allreduce", "fused", ["--steps", "30", "--warmup", "30"]),
+    ("small_int32", "reduce_scatter", "fused", ["--steps", "30", "--warmup", "30"]),
+    ("small_int32", "allgather", "fused", ["--steps", "30", "--warmup", "30"]),
+    ("small_int32", "ring_allreduce", "step", ["--steps", "30", "--warmup", "30"]),
 ] + [
     # message-size sweep: every size event-timed with the Infinity Cache flushed,
     # so that the events hold GPU time only (the cost model is fitted to these)
-    (f"sweep_{t}", coll, impl, ["--steps", "30", "--flush-mall"])
+    (f"sweep_{t}", coll, impl, ["--steps", "30", "--flush-mall", "--warmup", "30"])
     for t in (256, 262_144, 4_194_304, 67_108_864)
     for coll in ("ring_allreduce", "tree_allreduce", "allreduce")
     for impl in ("fused", "step")
@@ -581,8 +596,8 @@ def main():
               f"{world}): the N logical ranks are N buffers in one GPU's HBM; no figure "
               f"across several GPUs is produced.", file=sys.stderr)
         sys.exit(2)
-    if args.warmup + args.steps > MAX_CALLS:
-        print(f"--warmup + --steps must stay <= {MAX_CALLS} (values grow by N per call)",
+    if args.steps > MAX_CALLS:
+        print(f"--steps must stay <= {MAX_CALLS} (values grow by up to N per call)",
               file=sys.stderr)
         sys.exit(2)
 
