@@ -49,15 +49,15 @@ struct CostCoeff {
 };
 std::mutex g_cost_mu;
 CostCoeff g_cost[9][2] = {
-    {{7.35, 6570.0}, {3.43, 6665.0}},   // ring AllReduce: fused, step
-    {{7.35, 6477.0}, {3.43, 6649.0}},   // ReduceScatter
-    {{7.35, 5937.0}, {3.43, 7446.0}},   // AllGather
-    {{7.35, 5993.0}, {3.43, 5876.0}},   // Broadcast
-    {{7.35, 6570.0}, {3.16, 6088.0}},   // double-tree AllReduce
-    {{7.35, 6534.0}, {7.35, 6534.0}},   // Reduce (fused either way)
-    {{3.43, 5558.0}, {3.43, 5558.0}},   // Scatter (one step either way)
-    {{3.43, 5249.0}, {3.43, 5249.0}},   // Gather (one step either way)
-    {{3.43, 5904.0}, {3.43, 5904.0}},   // AllToAll (one kernel either way)
+    {{7.66, 6546.0}, {3.32, 6669.0}},   // ring AllReduce: fused, step
+    {{7.66, 6604.0}, {3.32, 6600.0}},   // ReduceScatter
+    {{7.66, 7247.0}, {3.32, 7451.0}},   // AllGather
+    {{7.66, 7247.0}, {3.32, 5846.0}},   // Broadcast
+    {{7.66, 6546.0}, {3.22, 6071.0}},   // double-tree AllReduce
+    {{7.66, 6706.0}, {7.66, 6706.0}},   // Reduce (fused either way)
+    {{3.32, 4224.0}, {3.32, 4224.0}},   // Scatter (one step either way)
+    {{3.32, 5556.0}, {3.32, 5556.0}},   // Gather (one step either way)
+    {{3.32, 5882.0}, {3.32, 5882.0}},   // AllToAll (one kernel either way)
 };
 
 bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_ALLTOALL; }
