@@ -139,7 +139,7 @@ typedef enum { AR_IMPL_FUSED = 0, AR_IMPL_STEP = 1 } ar_impl_t;
  * ReduceScatter then AllGather.  Afterwards every bufs[r] holds, at element
  * i of chunk c, the fold x[c+1][i] (+) ... (+) x[c][i] taken in ring order
  * (each hop: the receiving rank's own value (+) the incoming partial).
- * AR_IMPL_FUSED: one fold storing into every rank; from 17 ranks and 384 MiB
+ * AR_IMPL_FUSED: one fold storing into every rank; from 12 ranks and 384 MiB
  * of inputs (nranks * count * element size) up, the fused ReduceScatter and
  * then the fused AllGather (two launches, the same bits, faster there). */
 ar_status_t ar_ring_allreduce(void* const* bufs, int nranks, size_t count, ar_dtype_t dtype,
@@ -174,7 +174,7 @@ ar_status_t ar_broadcast(void* const* bufs, int nranks, size_t count, ar_dtype_t
  * role == rank, tree 1 handles [ceil(T/2), T) with role == N-1-rank.  Reduce
  * round k: role q (q mod 2^(k+1) == 0, q + 2^k < N) stores
  * own (+) value of role q + 2^k.  Every bufs[r] ends with role 0's result.
- * AR_IMPL_FUSED: one fold storing into every rank; from 17 ranks and 384 MiB
+ * AR_IMPL_FUSED: one fold storing into every rank; from 12 ranks and 384 MiB
  * of inputs up, the two trees' folds stored into their roots (rank 0, rank
  * N-1) and then both halves fanned out from there (two launches, the same
  * bits, faster there). */
@@ -240,7 +240,7 @@ ar_status_t ar_allreduce_choice(int nranks, size_t count, ar_dtype_t dtype,
 /* Kernel launches and HBM bytes of one call of `coll` under `impl` with these
  * arguments, as the library will run it: AR_IMPL_FUSED is one launch moving
  * every input once and every output once (2 N T s for an AllReduce), except
- * the AllReduces from 17 ranks and 384 MiB of inputs, which are two launches
+ * the AllReduces from 12 ranks and 384 MiB of inputs, which are two launches
  * moving (2 N + 1) T s; AR_IMPL_STEP is one launch per schedule step moving
  * 3 bytes per element of every reduce transfer (read both sides, write one)
  * and 2 per element of every copy transfer.  Reduce and AllToAll run their

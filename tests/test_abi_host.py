@@ -226,11 +226,11 @@ def _oracle_hbm_bytes(coll, impl, n, t, dtype):
 
 
 def _split(n, t, s):
-    """The fused AllReduces run in two launches from 17 ranks and 384 MiB of
+    """The fused AllReduces run in two launches from 12 ranks and 384 MiB of
     inputs up (the documented rule of ar.h): the ring as ReduceScatter then
     AllGather, the double tree as its folds into the two roots then their
     fan-out."""
-    return n >= 17 and n * t * s >= 384 << 20
+    return n >= 12 and n * t * s >= 384 << 20
 
 
 @pytest.mark.parametrize("coll", sorted(ORACLE_CALLS))
@@ -300,16 +300,18 @@ def test_launch_plan_arguments_are_validated():
 @pytest.mark.parametrize("n,t,dtype", [(64, 1_572_864, "float32"), (64, 1_572_863, "float32"),
                                        (32, 100_000_000, "float32"), (17, 5_921_371, "float32"),
                                        (17, 5_921_370, "float32"), (16, 100_000_000, "float32"),
+                                       (12, 8_388_608, "float32"), (12, 8_388_607, "float32"),
+                                       (11, 100_000_000, "float32"),
                                        (64, 1_048_576, "float32"), (64, 16_777_217, "float32"),
                                        (20, 10_066_330, "bfloat16"), (20, 10_066_329, "bfloat16"),
                                        (33, 4_194_304, "bfloat16")])
 def test_fused_allreduce_split_is_modelled(coll, n, t, dtype):
-    """From 17 ranks and 384 MiB of inputs the fused AllReduces are two
+    """From 12 ranks and 384 MiB of inputs the fused AllReduces are two
     launches moving (2N+1) T s bytes; below either bound one launch of 2N T s."""
     s = 2 if dtype == "bfloat16" else 4
     alpha, gbps = ar.get_cost_model(coll, "fused")
     split = _split(n, t, s)
-    assert split == (n >= 17 and n * t * s >= 402_653_184)
+    assert split == (n >= 12 and n * t * s >= 402_653_184)
     launches, nbytes = (2, (2 * n + 1) * t * s) if split else (1, 2 * n * t * s)
     want = launches * alpha + nbytes / (gbps * 1e3)
     assert ar.predict_time(coll, "fused", n, t, dtype) == pytest.approx(want, rel=1e-12)

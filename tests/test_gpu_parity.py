@@ -507,7 +507,7 @@ def test_zero_n64_reduce_scatter_then_allgather_and_broadcast():
 
 
 def test_split_ring_allreduce_many_ranks():
-    """From 17 ranks and 384 MiB of inputs the fused ring AllReduce runs as the
+    """From 12 ranks and 384 MiB of inputs the fused ring AllReduce runs as the
     fused ReduceScatter followed by the fan-out AllGather.  N=64 x 16,777,217
     float32 (ragged chunks): sampled windows against the oracle and whole
     buffers against the step implementation (the literal schedule); N=40 x
@@ -579,7 +579,7 @@ def test_split_ring_allreduce_many_ranks():
 
 
 def test_split_tree_allreduce_many_ranks():
-    """From 17 ranks and 384 MiB of inputs the fused double-tree AllReduce runs
+    """From 12 ranks and 384 MiB of inputs the fused double-tree AllReduce runs
     as both trees' folds stored into their roots (rank 0, rank N-1), then the
     two halves fanned out from those roots.  N=64 x 16,777,217 float32:
     sampled windows against the oracle (cuts at the halves' boundary) and
@@ -646,6 +646,28 @@ def test_split_tree_allreduce_many_ranks():
                             f"{odt} window {lo} rank {r}")
         assert _ranks_identical(bufs)
         del bufs, saved
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce"])
+def test_split_at_twelve_ranks_matches_the_step_schedule(coll):
+    """N=12 x 8,388,608 int32 (384 MiB of inputs, the smallest split size at
+    12 ranks): the two-launch fused AllReduce equals the literal schedule on
+    every element of every rank, and 8,388,607 (one launch) does too."""
+    for t in (8_388_608, 8_388_607):
+        outs = []
+        for impl in ("fused", "step"):
+            ar.set_impl(impl)
+            bufs = [workloads.device_rank("int_uniform", "int32", t, 41, r, DEV, {"lo": -1000, "hi": 1000})
+                    for r in range(12)]
+            announce(f"{coll} n=12 t={t} int32 impl={impl}")
+            getattr(ar, coll)(bufs)
+            torch.cuda.synchronize()
+            outs.append(bufs)
+        ar.set_impl("fused")
+        assert ar.launch_plan(coll, "fused", 12, t, "int32")[0] == (2 if t == 8_388_608 else 1)
+        assert all(torch.equal(x, y) for x, y in zip(*outs))
+        del outs
         torch.cuda.empty_cache()
 
 

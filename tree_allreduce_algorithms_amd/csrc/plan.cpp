@@ -292,7 +292,7 @@ int expected_steps(ar_collective_t coll, int n) {
 }
 
 bool allreduce_split(int n, uint64_t count, size_t isz) {
-  constexpr int kMinRanks = 17;
+  constexpr int kMinRanks = 12;
   constexpr uint64_t kMinInputBytes = 3ull << 27;   // 384 MiB
   return n >= kMinRanks && static_cast<uint64_t>(n) * count * isz >= kMinInputBytes;
 }

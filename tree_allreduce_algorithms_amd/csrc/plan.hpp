@@ -85,12 +85,13 @@ uint64_t impl_hbm_bytes(ar_collective_t coll, ar_impl_t impl, int n, uint64_t co
 // 09 section 5.2], and the first launch leaves exactly the value the one-pass
 // fold stores.  With many ranks the one-pass fold writes every tile into all
 // N buffers at once, which HBM serves poorly, while the copy writes one
-// buffer after another.  Measured on gfx950 (in-process A/B, float32, 17 to
-// 64 ranks): with 384 MiB to 4.8 GB of inputs the two launches are 1-13 %
-// faster than the one-pass fold for both algorithms, except the ring at 24
-// ranks and 805 MB (even); with exactly 256 MiB (the Infinity Cache's size)
-// they are 1-7 % slower for most rank counts; at 12 and 16 ranks (1.2 GB)
-// the one-pass folds tie.  So both split from 17 ranks and 384 MiB of inputs.
+// buffer after another.  Measured on gfx950 (in-process A/B, float32, warm
+// clocks): with 384 MiB to 4.8 GB of inputs the two launches are 1-13 %
+// faster than the one-pass folds from 16 to 64 ranks (ring at 24 ranks and
+// 805 MB: even), 1-9 % faster at 11-16 ranks, within 2 % at 8-10 and 8 %
+// slower at 6; with exactly 256 MiB (the Infinity Cache's size) they are
+// 1-7 % slower for most rank counts.  So both split from 12 ranks and
+// 384 MiB of inputs.
 bool allreduce_split(int n, uint64_t count, size_t isz);
 
 // Validation shared by every collective call.  `op` < 0 means "not used",
