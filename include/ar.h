@@ -130,7 +130,11 @@ typedef enum {
  *   AR_IMPL_FUSED  one pass: every element's N inputs are read once, folded
  *                  in the schedule's order (tiles staged through LDS, the
  *                  partials in registers), and the result is written once
- *                  per destination rank.
+ *                  per destination rank; the copies (AllGather, Broadcast)
+ *                  read each element once and write it into every other
+ *                  rank, one destination rank per pass.  The AllReduces of
+ *                  12 or more ranks and 384 MiB or more of inputs run as two
+ *                  such launches (see ar_ring_allreduce, ar_tree_allreduce).
  *   AR_IMPL_STEP   the schedule literally: one kernel launch per ring step or
  *                  tree round, each applying all of that step's transfers. */
 typedef enum { AR_IMPL_FUSED = 0, AR_IMPL_STEP = 1 } ar_impl_t;
