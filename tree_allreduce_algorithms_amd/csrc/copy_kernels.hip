@@ -183,10 +183,11 @@ __global__ __launch_bounds__(kBlock) void fanout_group_kernel(FanoutGroupArgs a)
 // of the fastest.
 constexpr uint64_t kFanoutGroupBytes = 12ull << 20;
 
-// Loads and stores of the grouped fan-out, measured on gfx950 against each
-// other: with two ranks (one pass, nothing read twice) the copy streams its
-// loads and stores through the caches; with more, the loads go through L2
-// for the later passes and the stores stream.
+// Loads and stores of the grouped fan-out, chosen by measurement on gfx950:
+// with two ranks (one pass, nothing read twice) the loads carry the
+// non-temporal hint and the stores go through the caches, as in a plain copy;
+// with more ranks the loads go through L2 (the later passes re-read them
+// there) and the stores carry the non-temporal hint.
 struct FanoutFlavour {
   int unroll;
   bool stream_loads;
