@@ -649,23 +649,34 @@ def test_split_tree_allreduce_many_ranks():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("aligned", [True, False], ids=["aligned16", "element_aligned"])
 @pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce"])
-def test_split_at_twelve_ranks_matches_the_step_schedule(coll):
+def test_split_at_twelve_ranks_matches_the_step_schedule(coll, aligned):
     """N=12 x 8,388,608 int32 (384 MiB of inputs, the smallest split size at
     12 ranks): the two-launch fused AllReduce equals the literal schedule on
-    every element of every rank, and 8,388,607 (one launch) does too."""
+    every element of every rank, and 8,388,607 (one launch) does too; with
+    16-byte aligned buffers (staged folds, grouped fan-out) and with buffers
+    aligned only to the element size (the element-at-a-time kernels)."""
+    n = 12
     for t in (8_388_608, 8_388_607):
         outs = []
         for impl in ("fused", "step"):
             ar.set_impl(impl)
-            bufs = [workloads.device_rank("int_uniform", "int32", t, 41, r, DEV, {"lo": -1000, "hi": 1000})
-                    for r in range(12)]
-            announce(f"{coll} n=12 t={t} int32 impl={impl}")
+            src = [workloads.device_rank("int_uniform", "int32", t, 41, r, DEV, {"lo": -1000, "hi": 1000})
+                   for r in range(n)]
+            if aligned:
+                bufs = src
+            else:
+                _, bufs = _element_aligned_views(n, t, "int32", [1 + r % 3 for r in range(n)])
+                for v, x in zip(bufs, src):
+                    v.copy_(x)
+                del src
+            announce(f"{coll} n={n} t={t} int32 impl={impl} aligned={aligned}")
             getattr(ar, coll)(bufs)
             torch.cuda.synchronize()
             outs.append(bufs)
         ar.set_impl("fused")
-        assert ar.launch_plan(coll, "fused", 12, t, "int32")[0] == (2 if t == 8_388_608 else 1)
+        assert ar.launch_plan(coll, "fused", n, t, "int32")[0] == (2 if t == 8_388_608 else 1)
         assert all(torch.equal(x, y) for x, y in zip(*outs))
         del outs
         torch.cuda.empty_cache()
