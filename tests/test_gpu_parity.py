@@ -682,6 +682,28 @@ def test_split_at_twelve_ranks_matches_the_step_schedule(coll, aligned):
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce"])
+def test_split_many_ranks_short_chunks_match_the_step_schedule(coll):
+    """N=64 x 1,572,864 float32 (384 MiB, the smallest split size at 64
+    ranks): the fan-out's groups then span many chunks (ring) or its halves
+    are shorter than a group (tree), so each pass writes one rank and skips the
+    tiles that rank owns.  Fused equals the literal schedule on every element."""
+    n, t = 64, 1_572_864
+    assert ar.launch_plan(coll, "fused", n, t, "float32")[0] == 2
+    outs = []
+    for impl in ("fused", "step"):
+        ar.set_impl(impl)
+        bufs = [workloads.device_rank("normal", "float32", t, 43, r, DEV, {"std": 1.0}) for r in range(n)]
+        announce(f"{coll} n={n} t={t} float32 impl={impl}")
+        getattr(ar, coll)(bufs)
+        torch.cuda.synchronize()
+        outs.append(bufs)
+    ar.set_impl("fused")
+    assert all(torch.equal(x, y) for x, y in zip(*outs))
+    del outs
+    torch.cuda.empty_cache()
+
+
 def test_zero_n64_reduce_scatter_gather_full_size():
     """N=64, T=16,777,217 float32 (ragged chunks): Reduce, Scatter and Gather
     to a root in the middle, on sampled windows; the ranks that the pages say
