@@ -59,9 +59,9 @@
  *           AR_ERROR_UNSUPPORTED       a valid request this build lacks;
  *           AR_ERROR_HIP               a kernel launch failed; the hipError_t
  *               is kept for ar_last_hip_error().  With the step
- *               implementation (or a fused ring AllReduce that runs as two
- *               launches) the launches before the failing one may already
- *               be enqueued, so the buffers are then unspecified.  (Faults
+ *               implementation (or a fused ring or tree AllReduce that runs
+ *               as two launches) the launches before the failing one may
+ *               already be enqueued, so the buffers are then unspecified.  (Faults
  *               during execution surface at the caller's next
  *               synchronisation.)
  *         count == 0 or nranks == 1 is a valid no-op (AR_SUCCESS, nothing

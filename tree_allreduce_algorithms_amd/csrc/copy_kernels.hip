@@ -312,10 +312,12 @@ hipError_t launch_fanout_chunks(const RankPtrs& ptrs, int n, uint64_t count, ar_
     const uint64_t groups = (all_slots + group_max - 1) / group_max;
     const uint64_t group = ((all_slots + groups - 1) / groups + 7) / 8 * 8;
     // A group inside one or two chunks has one source per tile, so pass j can
-    // write rank src + 1 + j: n - 1 passes, each one buffer.  A group over
-    // many small chunks keeps one destination per pass instead (pass j
-    // writes rank j, or j + 1 past a Broadcast's root; the tiles whose source
-    // is rank j have nothing to do).
+    // write rank src + 1 + j: n - 1 passes, each one buffer.  A Broadcast
+    // (one source for every chunk) always takes that order.  A group over
+    // many small chunks of an AllGather or the tree's halves keeps one
+    // destination per pass instead: pass j writes rank j, and the tiles whose
+    // source is rank j have nothing to do.  (The kernel's other order also
+    // skips a root, so either order is valid for any call.)
     a.rotate = (root >= 0 || slots * 2 >= group) ? 1 : 0;
     a.passes = (a.rotate || root >= 0) ? n - 1 : n;
     const uint64_t units = (all_slots + group - 1) / group * group * static_cast<uint64_t>(a.passes);
