@@ -572,8 +572,17 @@ SUITE = [
     ("zero_n64", "gather", "fused", ["--warmup", "600"]),
     ("zero_n64", "ring_allreduce", "fused", ["--warmup", "20"]),
     ("zero_n64", "tree_allreduce", "fused", ["--warmup", "20"]),
+    # the same with the Infinity Cache flushed before each call: a copy's
+    # source (one rank's worth, 67 MB here) otherwise stays in that cache
+    # from one back-to-back call to the next
+    ("zero_n64", "reduce_scatter", "fused", ["--flush-mall", "--warmup", "40"]),
+    ("zero_n64", "allgather", "fused", ["--flush-mall", "--warmup", "40"]),
+    ("zero_n64", "broadcast", "fused", ["--flush-mall", "--warmup", "40"]),
+    ("zero_n64", "ring_allreduce", "fused", ["--flush-mall", "--warmup", "20"]),
+    ("zero_n64", "tree_allreduce", "fused", ["--flush-mall", "--warmup", "20"]),
     ("large_grad_fp32", "reduce", "fused", ["--warmup", "15"]),
     ("moe_alltoall", "alltoall", "fused", ["--warmup", "80"]),
+    ("moe_alltoall", "alltoall", "fused", ["--flush-mall", "--warmup", "80"]),
     ("small_int32", "ring_allreduce", "fused", ["--steps", "30", "--warmup", "30"]),
     ("small_int32", "reduce_scatter", "fused", ["--steps", "30", "--warmup", "30"]),
     ("small_int32", "allgather", "fused", ["--steps", "30", "--warmup", "30"]),
