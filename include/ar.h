@@ -315,6 +315,20 @@ int ar_last_hip_error(void);
 /* AR_VERSION of the loaded library. */
 int ar_version(void);
 
+/* ---- testing ---------------------------------------------------------------- */
+
+/* For callers' tests of their AR_ERROR_HIP handling (the error path of the
+ * "Errors" paragraph above, which a healthy GPU never takes): the k-th kernel
+ * launch the library attempts from now on (k >= 1; a collective call makes
+ * one launch, or one per step with AR_IMPL_STEP, or two for the two-launch
+ * AllReduces, and none when it is a no-op) reports hipErrorLaunchFailure
+ * instead of being enqueued.  That call then returns AR_ERROR_HIP with nothing more enqueued,
+ * ar_last_hip_error() gives hipErrorLaunchFailure on its thread, the
+ * launches it made before stay enqueued, and the counters are not updated.
+ * The injection is spent by that launch; k == 0 disarms it.  Process-wide;
+ * host only; AR_ERROR_INVALID_ARGUMENT for k < 0. */
+ar_status_t ar_debug_fail_launch(int k);
+
 #ifdef __cplusplus
 }
 #endif

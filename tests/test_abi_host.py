@@ -14,6 +14,7 @@ ever launched and fake device addresses are never dereferenced.
 import ctypes
 import os
 import re
+import threading
 
 import numpy as np
 import pytest
@@ -151,6 +152,55 @@ def test_invalid_arguments(name):
     del keep
 
 
+# An armed launch-failure injection fails a call's first launch before
+# anything reaches the HIP runtime, so these calls need no GPU either.
+HIP_ERROR_LAUNCH_FAILURE = 719   # hipErrorLaunchFailure in HIP's runtime API
+
+
+@pytest.mark.parametrize("impl", ["fused", "step"])
+@pytest.mark.parametrize("name", ALL + ["allreduce"])
+def test_injected_launch_failure_is_reported(name, impl):
+    """ar_debug_fail_launch(1): the call's first launch reports
+    hipErrorLaunchFailure, so the call returns AR_ERROR_HIP, keeps the error
+    for ar_last_hip_error() on its own thread only, and leaves the counters
+    as they were."""
+    lib = ar.lib()
+    old = ar.get_impl()
+    try:
+        ar.set_impl(impl)
+        ar.reset_counters()
+        ar.debug_fail_launch(1)
+        assert _call(name, _fake(4), count=64, root=1) == binding.HIP_ERROR
+        assert lib.ar_last_hip_error() == HIP_ERROR_LAUNCH_FAILURE
+        assert ar.counters(4) == ([0] * 4, [0] * 4, 0)
+        seen = []
+        th = threading.Thread(target=lambda: seen.append(lib.ar_last_hip_error()))
+        th.start()
+        th.join()
+        assert seen == [0]
+        with pytest.raises(ar.ArError, match=f"hipError_t {HIP_ERROR_LAUNCH_FAILURE}"):
+            ar.debug_fail_launch(1)
+            binding._check(_call(name, _fake(4), count=64, root=1), name)
+    finally:
+        ar.debug_fail_launch(0)
+        ar.set_impl(old)
+
+
+def test_launch_failure_injection_spares_argument_errors_and_no_ops():
+    """Calls that fail validation or are no-ops make no launch: they return
+    as without the injection, which stays armed for the next launch."""
+    lib = ar.lib()
+    try:
+        assert lib.ar_debug_fail_launch(-1) == binding.INVALID_ARGUMENT
+        assert lib.ar_debug_fail_launch(1) == binding.SUCCESS
+        assert _call("ring_allreduce", _fake(4, offset=2)) == binding.INVALID_ARGUMENT
+        assert _call("ring_allreduce", _fake(4), count=0) == binding.SUCCESS
+        assert _call("ring_allreduce", _fake(1), count=64) == binding.SUCCESS
+        assert _call("ring_allreduce", _fake(4), count=64) == binding.HIP_ERROR
+    finally:
+        assert lib.ar_debug_fail_launch(0) == binding.SUCCESS
+
+
 def test_bfloat16_needs_only_2_byte_alignment_to_validate():
     # odd addresses fail for every dtype; 2-byte offsets fail for 4-byte types
     assert _call("allgather", _fake(2, offset=1), dtype="bfloat16") == binding.INVALID_ARGUMENT
@@ -182,7 +232,12 @@ def test_impl_switch_and_status_strings():
     lib = ar.lib()
     assert lib.ar_status_string(0) == b"success"
     assert lib.ar_status_string(1) == b"invalid argument"
-    assert lib.ar_last_hip_error() == 0
+    # no AR_ERROR_HIP on a fresh thread (the value is kept per thread)
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(lib.ar_last_hip_error()))
+    th.start()
+    th.join()
+    assert seen == [0]
 
 
 def test_host_helpers_reject_bad_arguments():

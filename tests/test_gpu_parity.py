@@ -1009,6 +1009,57 @@ def test_rank_buffers_match_the_free_functions():
     with pytest.raises(ValueError):
         ar.RankBuffers([torch.zeros(4, device=DEV), torch.zeros(5, device=DEV)])
 
+
+def test_injected_launch_failure_leaves_earlier_launches_enqueued():
+    """ar_debug_fail_launch on real buffers.  The two-launch ring AllReduce
+    (17 ranks x 5,921,371 int32, 384 MiB and up) with its second launch
+    failing returns AR_ERROR_HIP after its ReduceScatter ran: every owner's
+    chunk equals what a fused ReduceScatter gives on the same inputs, and the
+    counters are untouched.  A step-implementation AllReduce whose third
+    launch fails reports the same.  After each failure the injection is spent
+    and the next call matches the oracle."""
+    n, t = 17, 5_921_371
+
+    def draw():
+        return [workloads.device_rank("int_uniform", "int32", t, 31, r, DEV, {"lo": -100, "hi": 100})
+                for r in range(n)]
+
+    small = workloads.host_inputs(4, 1000, "int32", "int_uniform", 37, {"lo": -100, "hi": 100})
+    try:
+        ar.set_impl("fused")
+        a, b = draw(), draw()
+        ar.reset_counters()
+        ar.debug_fail_launch(2)
+        announce(f"ring_allreduce n={n} t={t} int32, second launch failing")
+        with pytest.raises(ar.ArError) as err:
+            ar.ring_allreduce(a)
+        assert err.value.status == binding.HIP_ERROR
+        assert ar.lib().ar_last_hip_error() == 719   # hipErrorLaunchFailure
+        assert ar.counters(n) == ([0] * n, [0] * n, 0)
+        ar.reduce_scatter(b)
+        torch.cuda.synchronize()
+        for c, (lo, hi) in enumerate(oracle.chunk_layout(n, t)):
+            assert torch.equal(a[c][lo:hi], b[c][lo:hi]), f"owner chunk {c}"
+        del a, b
+        torch.cuda.empty_cache()
+        compare_collective("ring_allreduce", small, "int32", "sum", 0, impls=("fused",))
+
+        ar.set_impl("step")
+        bufs = to_dev(small, "int32")
+        ar.reset_counters()
+        ar.debug_fail_launch(3)
+        announce("ring_allreduce impl=step n=4 t=1000 int32, third launch failing")
+        with pytest.raises(ar.ArError) as err:
+            ar.ring_allreduce(bufs)
+        assert err.value.status == binding.HIP_ERROR
+        torch.cuda.synchronize()
+        assert ar.counters(4) == ([0] * 4, [0] * 4, 0)
+        compare_collective("ring_allreduce", small, "int32", "sum", 0, impls=("step",))
+    finally:
+        ar.debug_fail_launch(0)
+        ar.set_impl("fused")
+
+
 @pytest.mark.parametrize("unroll", ["1", "2", "4"])
 def test_unroll_override_is_bit_identical(unroll):
     """AR_TUNE_UNROLL only regroups the fan-out's packs: forced to 1, 2 or 4

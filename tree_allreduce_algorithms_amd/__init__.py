@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     chunk_range,
     chunk_size,
     counters,
+    debug_fail_launch,
     expected_bytes,
     expected_steps,
     gather,

@@ -53,6 +53,7 @@ SIGNATURES = {
     "ar_status_string": (ctypes.c_char_p, [_I]),
     "ar_last_hip_error": (_I, []),
     "ar_version": (_I, []),
+    "ar_debug_fail_launch": (_I, [_I]),
 }
 
 _lib = None
@@ -410,6 +411,13 @@ def reset_counters():
 
 def set_impl(impl):
     _check(lib().ar_set_impl(IMPLS[impl]), "set_impl")
+
+
+def debug_fail_launch(k):
+    """Make the k-th kernel launch from now (k >= 1) fail with
+    hipErrorLaunchFailure instead of being enqueued; 0 disarms.  For tests
+    of the AR_ERROR_HIP path (the call raises ArError)."""
+    _check(lib().ar_debug_fail_launch(int(k)), "debug_fail_launch")
 
 
 def get_impl():

@@ -31,6 +31,21 @@ std::atomic<int> g_impl{static_cast<int>(impl_from_env())};
 
 thread_local int t_last_hip_error = 0;
 
+// Launch-failure injection (ar_debug_fail_launch): while the counter is
+// positive, every launch the library is about to make takes one from it, and
+// the launch that takes it from 1 to 0 returns hipErrorLaunchFailure without
+// reaching the HIP runtime.
+std::atomic<int> g_fail_launch{0};
+
+template <class F>
+hipError_t enqueue(F&& launch_fn) {
+  int k = g_fail_launch.load(std::memory_order_relaxed);
+  while (k > 0 && !g_fail_launch.compare_exchange_weak(k, k - 1, std::memory_order_relaxed)) {
+  }
+  if (k == 1) return hipErrorLaunchFailure;
+  return launch_fn();
+}
+
 // Cost model coefficients (alpha_us per launch, gbps of HBM traffic) per
 // collective and implementation.  The AllReduce pairs are the least-squares
 // fit of launches * alpha + bytes / gbps to the N=4 float32 message-size sweep
@@ -141,14 +156,14 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
   if (coll == AR_REDUCE) {
     // one implementation: the partials of the rounds live in registers, so
     // no rank other than the root is written
-    err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, root, false, vec, stream);
+    err = enqueue([&] { return ar::launch_tree_fold(ptrs, n, count, dtype, aop, root, false, vec, stream); });
   } else if (coll == AR_ALLTOALL) {
-    err = ar::launch_alltoall(ptrs, n, count, dtype, vec, stream);
+    err = enqueue([&] { return ar::launch_alltoall(ptrs, n, count, dtype, vec, stream); });
   } else if (impl == AR_IMPL_STEP || coll == AR_SCATTER || coll == AR_GATHER) {
     // the literal schedule: one launch per step (the schedule is built only here)
     const std::vector<ar::Step> sched = ar::schedule_for(coll, n, count, root < 0 ? 0 : root);
     for (const ar::Step& s : sched) {
-      err = ar::launch_step(ptrs, s, dtype, aop, vec, stream);
+      err = enqueue([&] { return ar::launch_step(ptrs, s, dtype, aop, vec, stream); });
       if (err != hipSuccess) break;
     }
   } else {
@@ -158,30 +173,32 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
           // fused ReduceScatter, then the owners' chunks fanned out: the same
           // bits as the one-pass fold (AllReduce = AllGather after
           // ReduceScatter), faster for many ranks
-          err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, vec, stream);
-          if (err == hipSuccess) err = ar::launch_fanout(ptrs, n, count, dtype, false, 0, vec, stream);
+          err = enqueue([&] { return ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, vec, stream); });
+          if (err == hipSuccess)
+            err = enqueue([&] { return ar::launch_fanout(ptrs, n, count, dtype, false, 0, vec, stream); });
         } else {
-          err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, true, vec, stream);
+          err = enqueue([&] { return ar::launch_ring_fold(ptrs, n, count, dtype, aop, true, vec, stream); });
         }
         break;
       case AR_REDUCE_SCATTER:
-        err = ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, vec, stream);
+        err = enqueue([&] { return ar::launch_ring_fold(ptrs, n, count, dtype, aop, false, vec, stream); });
         break;
       case AR_ALLGATHER:
-        err = ar::launch_fanout(ptrs, n, count, dtype, false, 0, vec, stream);
+        err = enqueue([&] { return ar::launch_fanout(ptrs, n, count, dtype, false, 0, vec, stream); });
         break;
       case AR_BROADCAST:
-        err = ar::launch_fanout(ptrs, n, count, dtype, true, root, vec, stream);
+        err = enqueue([&] { return ar::launch_fanout(ptrs, n, count, dtype, true, root, vec, stream); });
         break;
       case AR_TREE_ALLREDUCE:
         if (ar::allreduce_split(n, count, ar::itemsize(dtype))) {
           // both trees' folds stored into their roots, then each root's half
           // fanned out: the reduce and broadcast passes, the same bits as the
           // one-pass fold, faster for many ranks
-          err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, true, vec, stream);
-          if (err == hipSuccess) err = ar::launch_tree_broadcast(ptrs, n, count, dtype, vec, stream);
+          err = enqueue([&] { return ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, true, vec, stream); });
+          if (err == hipSuccess)
+            err = enqueue([&] { return ar::launch_tree_broadcast(ptrs, n, count, dtype, vec, stream); });
         } else {
-          err = ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, false, vec, stream);
+          err = enqueue([&] { return ar::launch_tree_fold(ptrs, n, count, dtype, aop, -1, false, vec, stream); });
         }
         break;
       default:   // Reduce, Scatter, Gather and AllToAll are dispatched above
@@ -379,6 +396,12 @@ const char* ar_status_string(ar_status_t status) {
 }
 
 int ar_last_hip_error(void) { return t_last_hip_error; }
+
+ar_status_t ar_debug_fail_launch(int k) {
+  if (k < 0) return AR_ERROR_INVALID_ARGUMENT;
+  g_fail_launch.store(k);
+  return AR_SUCCESS;
+}
 
 int ar_version(void) { return AR_VERSION; }
 
