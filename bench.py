@@ -141,17 +141,33 @@ def _code_only(text):
     return "\n".join(line for line in lines if line.strip())
 
 
-def kernel_source_hash(kernel=None):
+def _local_includes(code):
+    return re.findall(r'^\s*#\s*include\s+"([^"]+)"', code, re.M)
+
+
+def kernel_source_hash(kernel=None, csrc=None):
     """sha256 over the device code a kernel is built from (comments and blank
-    lines removed): its own source file plus every shared header (all device
-    sources when kernel is None), in name order."""
-    csrc = os.path.join(ROOT, "tree_allreduce_algorithms_amd", "csrc")
+    lines removed): its own source file (every .hip file when kernel is None)
+    plus the headers of the same directory that it includes, directly or
+    through one another, in name order."""
+    csrc = csrc or os.path.join(ROOT, "tree_allreduce_algorithms_amd", "csrc")
     own = KERNEL_FILE.get(kernel)
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith(".hpp") or (name.endswith(".hip") and (own is None or name == own)):
+    code = {}
+
+    def read(name):
+        if name not in code:
             with open(os.path.join(csrc, name), encoding="utf-8") as f:
-                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
+                code[name] = _code_only(f.read())
+            for inc in _local_includes(code[name]):
+                if os.path.exists(os.path.join(csrc, inc)):
+                    read(inc)
+
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith(".hip") and (own is None or name == own):
+            read(name)
+    h = hashlib.sha256()
+    for name in sorted(code):
+        h.update(name.encode() + b"\0" + code[name].encode())
     return h.hexdigest()
 
 

@@ -71,6 +71,15 @@
  *         schedule (each transfer of k elements adds k * element size to the
  *         sender's `sent` and the receiver's `recv`) and its schedule steps
  *         to process-wide counters, whatever implementation runs.
+ * Debug   with the environment variable AR_DEBUG set (and not "0") when the
+ *         library loads, every call with work to do first builds the logical
+ *         schedule it follows and checks it: every transfer inside the
+ *         buffers and between two distinct ranks, no transfer of a step
+ *         writing what another one of the step reads or writes [the ring's
+ *         within-step disjointness, L09 4.3], the documented step count, and
+ *         per-rank bytes equal to what the counters add.  A violation, which
+ *         would be a defect of this library, is printed to stderr and aborts
+ *         the process; nothing of that call is enqueued.
  */
 #ifndef AR_H
 #define AR_H

@@ -12,6 +12,12 @@
 //    swap);
 //  * the closed-form per-rank byte counts equal the counts summed over the
 //    schedule, and the step count is the documented one;
+//  * the library's own check, schedule_violation() (what AR_DEBUG=1 runs
+//    before every call), accepts every schedule above, and names the fault
+//    in schedules with a planted one (two writes of the same elements, a
+//    write of what another transfer reads, a range past the buffer, a
+//    transfer from a rank to itself, a missing step, bytes that differ from
+//    the closed forms);
 //  * the chunk bounds tile [0, count) in order;
 //  * validate() accepts good arguments and rejects NULL entries, misaligned
 //    or overlapping buffers, out-of-range roots and sizes whose byte length
@@ -19,10 +25,12 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <random>
 #include <vector>
 
 #include "plan.hpp"
+#include "plan_check.hpp"
 
 namespace {
 
@@ -72,6 +80,9 @@ void check_schedule(ar_collective_t coll, int n, uint64_t count, int root) {
       }
     }
   }
+  const char* why = ar::schedule_violation(coll, steps, n, count, root);
+  CHECK(why == nullptr, "coll %d n %d count %llu root %d: schedule_violation: %s", coll, n,
+        (unsigned long long)count, root, why ? why : "");
   for (size_t isz : {size_t(2), size_t(4)}) {
     std::vector<uint64_t> s1(n, 0), r1(n, 0), s2(n, 0), r2(n, 0);
     ar::count_bytes(steps, isz, s1.data(), r1.data());
@@ -82,6 +93,51 @@ void check_schedule(ar_collective_t coll, int n, uint64_t count, int root) {
             coll, n, (unsigned long long)count, root, r, (unsigned long long)s1[r],
             (unsigned long long)r1[r], (unsigned long long)s2[r], (unsigned long long)r2[r]);
   }
+}
+
+// schedule_violation() on schedules with one planted fault each: it must
+// report the fault named by `expect` (a substring of its message).
+void planted(const char* what, ar_collective_t coll, const std::vector<ar::Step>& steps, int n,
+             uint64_t count, const char* expect) {
+  const char* why = ar::schedule_violation(coll, steps, n, count, 0);
+  CHECK(why != nullptr && std::strstr(why, expect) != nullptr, "%s: got \"%s\"", what,
+        why ? why : "(accepted)");
+}
+
+void check_planted() {
+  const int n = 4;
+  const uint64_t t = 16;
+  const std::vector<ar::Step> rs = ar::ring_reduce_scatter_schedule(n, t);
+  CHECK(ar::schedule_violation(AR_REDUCE_SCATTER, rs, n, t, 0) == nullptr, "unplanted schedule");
+  std::vector<ar::Step> bad = rs;
+  bad[0].xfers.push_back(bad[0].xfers[0]);
+  planted("a transfer repeated in its step", AR_REDUCE_SCATTER, bad, n, t, "write the same");
+  bad = rs;
+  ar::Transfer& x = bad[1].xfers[1];
+  x.src = bad[1].xfers[0].dst;   // reads what transfer 0 of the step writes
+  x.lo = bad[1].xfers[0].lo;
+  x.hi = bad[1].xfers[0].hi;
+  if (x.dst == x.src) x.dst = (x.src + 2) % n;
+  planted("a transfer reading what another one writes", AR_REDUCE_SCATTER, bad, n, t,
+          "writes what another one reads");
+  bad = rs;
+  bad[0].xfers[0].hi = t + 1;
+  planted("a range past the buffer", AR_REDUCE_SCATTER, bad, n, t, "outside the buffer");
+  bad = rs;
+  bad[0].xfers[0].dst = bad[0].xfers[0].src;
+  planted("a transfer to its own rank", AR_REDUCE_SCATTER, bad, n, t, "to itself");
+  bad = rs;
+  bad.pop_back();
+  planted("a missing step", AR_REDUCE_SCATTER, bad, n, t, "step count");
+  bad = rs;
+  bad[2].xfers[3].hi -= 1;
+  planted("a shortened transfer", AR_REDUCE_SCATTER, bad, n, t, "closed forms");
+  // a copy step's transfer widened to its destination's whole buffer, part
+  // of which the transfer out of that rank reads in the same step
+  std::vector<ar::Step> ag = ar::ring_allgather_schedule(n, t);
+  ag[0].xfers[2].lo = 0;
+  ag[0].xfers[2].hi = t;
+  planted("a widened copy", AR_ALLGATHER, ag, n, t, "writes what another one reads");
 }
 
 void check_chunks(int n, uint64_t count) {
@@ -150,6 +206,7 @@ int main() {
     }
   }
   check_validate();
+  check_planted();
   if (g_failures) {
     std::printf("%d checks failed\n", g_failures);
     return 1;

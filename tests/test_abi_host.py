@@ -14,6 +14,8 @@ ever launched and fake device addresses are never dereferenced.
 import ctypes
 import os
 import re
+import subprocess
+import sys
 import threading
 
 import numpy as np
@@ -184,6 +186,43 @@ def test_injected_launch_failure_is_reported(name, impl):
     finally:
         ar.debug_fail_launch(0)
         ar.set_impl(old)
+
+
+_DEBUG_SCRIPT = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import tree_allreduce_algorithms_amd as ar
+from tree_allreduce_algorithms_amd import binding
+names = ["ring_allreduce", "reduce_scatter", "allgather", "broadcast", "tree_allreduce", "reduce",
+         "scatter", "gather", "alltoall", "allreduce"]
+bad, calls = [], 0
+for impl in ("fused", "step"):
+    ar.set_impl(impl)
+    for n, t in ((2, 5), (5, 23), (12, 1000), (17, 5_921_371), (64, 16_777_217)):
+        ptrs = [0x7F0000000000 + r * (1 << 27) for r in range(n)]
+        for name in names:
+            count = t - t % n if name == "alltoall" else t
+            ar.debug_fail_launch(1)
+            status = binding.raw_call(name, ptrs, count, "float32", op="sum", root=n - 1)
+            calls += 1
+            if status != binding.HIP_ERROR:
+                bad.append((impl, n, t, name, status))
+ar.debug_fail_launch(0)
+print("BAD", bad) if bad else print("OK", calls)
+"""
+
+
+def test_debug_mode_checks_each_schedule_before_enqueuing():
+    """With AR_DEBUG=1 at load, a call with work builds the schedule it
+    follows and checks it (schedule_violation, pinned by the sanitized host
+    check) before its first launch, aborting on a violation.  The library's
+    schedules pass for every collective and implementation at 2 to 64 ranks,
+    ragged sizes included, and each call goes on to its launch (here an
+    injected failure, so no GPU is needed)."""
+    proc = subprocess.run([sys.executable, "-c", _DEBUG_SCRIPT, ROOT], capture_output=True,
+                          text=True, timeout=300, env={**os.environ, "AR_DEBUG": "1"})
+    assert proc.returncode == 0, proc.stderr[-3000:]
+    assert proc.stdout.split() == ["OK", "100"], proc.stdout[-3000:]
 
 
 def test_launch_failure_injection_spares_argument_errors_and_no_ops():

@@ -178,3 +178,18 @@ def test_kernel_hash_ignores_comments_only():
     assert bench._code_only(code) == 'int a = 1;\nconst char* s = "// not a comment";\nchar c = \'/\';'
     assert bench._code_only("x = 1;  // a\n") == bench._code_only("x = 1;  // b\n")
     assert bench._code_only("x = 1;\n") != bench._code_only("x = 2;\n")
+
+
+def test_kernel_hash_follows_includes(tmp_path):
+    """The hash covers a kernel's source and the headers it includes,
+    directly or through one another; a header no kernel includes (host-only
+    code) leaves it unchanged."""
+    (tmp_path / "a_kernels.hip").write_text('#include "common.hpp"\nint k;\n')
+    (tmp_path / "common.hpp").write_text('#include "deep.hpp"\n#include <vector>\nint c;\n')
+    (tmp_path / "deep.hpp").write_text("int d;\n")
+    (tmp_path / "host_only.hpp").write_text("int h;\n")
+    h0 = bench.kernel_source_hash(None, csrc=str(tmp_path))
+    (tmp_path / "host_only.hpp").write_text("int h2;\n")
+    assert bench.kernel_source_hash(None, csrc=str(tmp_path)) == h0
+    (tmp_path / "deep.hpp").write_text("int d2;\n")
+    assert bench.kernel_source_hash(None, csrc=str(tmp_path)) != h0

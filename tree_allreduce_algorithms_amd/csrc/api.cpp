@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -15,6 +16,7 @@
 #include "ar.h"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "plan_check.hpp"
 
 namespace {
 
@@ -28,6 +30,26 @@ ar_impl_t impl_from_env() {
   return (v != nullptr && std::strcmp(v, "step") == 0) ? AR_IMPL_STEP : AR_IMPL_FUSED;
 }
 std::atomic<int> g_impl{static_cast<int>(impl_from_env())};
+
+// AR_DEBUG (set and not "0" at load): before enqueuing anything, every call
+// with work to do builds the logical schedule it follows and checks it with
+// schedule_violation(); a violation (a defect of this library) is printed
+// and aborts the process.
+bool debug_from_env() {
+  const char* v = std::getenv("AR_DEBUG");
+  return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
+const bool g_debug = debug_from_env();
+
+void debug_check_schedule(ar_collective_t coll, int n, size_t count, int root) {
+  const int r = root < 0 ? 0 : root;
+  const char* why = ar::schedule_violation(coll, ar::schedule_for(coll, n, count, r), n, count, r);
+  if (why != nullptr) {
+    std::fprintf(stderr, "libar: AR_DEBUG: the schedule of collective %d (N=%d, T=%zu, root %d) "
+                 "fails its check: %s\n", static_cast<int>(coll), n, count, r, why);
+    std::abort();
+  }
+}
 
 thread_local int t_last_hip_error = 0;
 
@@ -129,6 +151,8 @@ ar_status_t run(ar_collective_t coll, void* const* bufs, int n, size_t count, ar
     add_counters(coll, n, count, root, ar::itemsize(dtype));
     return AR_SUCCESS;
   }
+
+  if (g_debug) debug_check_schedule(coll, n, count, root);
 
   ar::RankPtrs ptrs;
   std::memset(&ptrs, 0, sizeof(ptrs));

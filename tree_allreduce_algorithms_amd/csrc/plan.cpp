@@ -8,6 +8,7 @@
 // 4.3.2 (two trees, half the data each), read as two binomial trees, the
 // second on mirrored roles.
 #include "plan.hpp"
+#include "plan_check.hpp"
 
 #include <algorithm>
 #include <utility>
@@ -360,6 +361,51 @@ ar_status_t validate(void* const* bufs, int n, size_t count, int dtype, int op, 
       if (order[i].first + bytes > order[i + 1].first) return AR_ERROR_INVALID_ARGUMENT;
   }
   return AR_SUCCESS;
+}
+
+namespace {
+
+// Transfers a and b touch overlapping elements of ranks ra and rb.
+bool collide(const Transfer& a, int ra, const Transfer& b, int rb) {
+  return ra == rb && a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+}  // namespace
+
+const char* schedule_violation(ar_collective_t coll, const std::vector<Step>& steps, int n,
+                               uint64_t count, int root) {
+  if (n < 1 || n > AR_MAX_RANKS) return "rank count out of range";
+  if (n > 1 && count > 0 && static_cast<int>(steps.size()) != expected_steps(coll, n))
+    return "the step count differs from the documented one";
+  for (const Step& s : steps) {
+    for (const Transfer& t : s.xfers) {
+      if (t.src < 0 || t.src >= n || t.dst < 0 || t.dst >= n || t.src == t.dst)
+        return "a transfer between ranks out of range or from a rank to itself";
+      if (t.lo > t.hi || t.hi > count) return "a transfer outside the buffer";
+    }
+    if (coll == AR_ALLTOALL) continue;
+    // a transfer writes its destination's range (and reads it too when the
+    // step reduces), and reads its source's range
+    for (size_t i = 0; i < s.xfers.size(); ++i) {
+      const Transfer& w = s.xfers[i];
+      for (size_t j = 0; j < s.xfers.size(); ++j) {
+        if (i == j) continue;
+        const Transfer& o = s.xfers[j];
+        if (collide(w, w.dst, o, o.dst)) return "two transfers of a step write the same elements";
+        if (collide(w, w.dst, o, o.src)) return "a transfer of a step writes what another one reads";
+      }
+    }
+  }
+  uint64_t sent[AR_MAX_RANKS] = {};
+  uint64_t recv[AR_MAX_RANKS] = {};
+  uint64_t want_sent[AR_MAX_RANKS];
+  uint64_t want_recv[AR_MAX_RANKS];
+  count_bytes(steps, 1, sent, recv);
+  logical_bytes(coll, n, count, root, 1, want_sent, want_recv);
+  for (int r = 0; r < n; ++r)
+    if (sent[r] != want_sent[r] || recv[r] != want_recv[r])
+      return "the schedule's bytes differ from the counters' closed forms";
+  return nullptr;
 }
 
 }  // namespace ar
