@@ -313,6 +313,68 @@ def test_concurrent_streams_keep_their_own_order():
             assert_same(to_host(h.tensors[r], dt)[lo:hi], w[r][lo:hi], dt, f"{dt} rank {r}")
 
 
+def test_host_threads_share_the_library():
+    """Four host threads, each with its own stream and rank buffers, call the
+    library at the same time (ctypes releases the interpreter lock during a
+    call): every thread's buffers end as the oracle's sequence of calls
+    leaves them, and the process-wide byte and step counters hold exactly
+    the sum over all threads' calls."""
+    import threading
+    specs = [(4, 100_003, "float32", 71, "ring_allreduce"), (6, 77_777, "int32", 72, "tree_allreduce"),
+             (8, 50_021, "bfloat16", 73, "allgather"), (3, 64_000, "float32", 74, "broadcast")]
+    calls = 6
+    plans = []
+    for n, t, dt, seed, coll in specs:
+        dist = "int_uniform" if dt == "int32" else "normal"
+        x = workloads.host_inputs(n, t, dt, dist, seed, _params(dist, n))
+        want = x
+        for _ in range(calls):   # int32 values wrap; floats stay finite at this scale
+            want = CALLS[coll][1](want, "max" if coll != "allgather" else None, dt, 1).bufs
+        plans.append((n, t, dt, coll, x, want))
+    streams = [torch.cuda.Stream() for _ in specs]
+    handles = [ar.RankBuffers(to_dev(x, dt), stream=st_)
+               for (n, t, dt, coll, x, _), st_ in zip(plans, streams)]
+    torch.cuda.synchronize()
+    ar.set_impl("fused")
+    ar.reset_counters()
+    errors = []
+
+    def work(h, coll):
+        try:
+            for _ in range(calls):
+                if coll == "broadcast":
+                    h.broadcast(root=1)
+                elif coll == "allgather":
+                    h.allgather()
+                else:
+                    getattr(h, coll)(op="max")
+        except Exception as e:   # reported after the join
+            errors.append(e)
+
+    announce("four host threads, one stream each")
+    threads = [threading.Thread(target=work, args=(h, p[3])) for h, p in zip(handles, plans)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    for st_ in streams:
+        st_.synchronize()
+    assert not errors, errors
+    total_sent = [0] * 8
+    total_recv = [0] * 8
+    total_steps = 0
+    for h, (n, t, dt, coll, _, want) in zip(handles, plans):
+        for r in range(n):
+            assert_same(to_host(h.tensors[r], dt), want[r], dt, f"{coll} {dt} rank {r}")
+        es, er = ar.expected_bytes(coll, n, t, dt, root=1)
+        for r in range(n):
+            total_sent[r] += calls * es[r]
+            total_recv[r] += calls * er[r]
+        total_steps += calls * ar.expected_steps(coll, n)
+    sent, recv, steps = ar.counters(8)
+    assert (sent, recv, steps) == (total_sent, total_recv, total_steps)
+
+
 def test_non_default_stream():
     n, t = 4, 65_537
     x = workloads.host_inputs(n, t, "float32", "normal", 41, {"std": 1.0})
