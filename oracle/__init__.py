@@ -31,7 +31,9 @@ int32 brute force, hand-derived order-revealing fp32 examples, the worked
 examples the pages print, an independently written 0-based schedule from the
 Lecture 09 lab / Chapter 4 pseudo-code on rotated ranks, the exactly rounded
 sum (``math.fsum``) within the recursive-summation bound, the pages' byte and
-step counts, and torch's CPU bfloat16 conversion.  Two readings are this
+step counts, torch's CPU bfloat16 conversion, the order-free maximum and
+minimum over the rank axis for MAX and MIN, the per-element fold order for
+PROD, and planted mistakes that each of these must catch.  Two readings are this
 package's own because the pages leave them open: the ragged chunk layout and
 the double-tree shape and split.  No page value can fix them; the oracle's
 implementation of each is pinned independently (chunks covering every element
