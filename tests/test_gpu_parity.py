@@ -640,6 +640,41 @@ def test_split_ring_allreduce_many_ranks():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("n,t,dtype", [
+    (3, 100_663_296, "int32"),      # exactly 384 MiB per rank: chunks in pairs, N odd
+    (3, 100_663_295, "int32"),      # one element less: chunk after chunk
+    (11, 100_663_297, "float32"),   # pairs, N odd, ragged chunks, below the split
+    (2, 201_326_593, "bfloat16"),   # pairs, one pair
+])
+def test_one_pass_allreduce_in_pairs_of_chunks(n, t, dtype):
+    """From 384 MiB per rank the one-pass ring AllReduce deals its blocks over
+    two chunks at a time.  On both sides of that size, for odd N (the last
+    pair's second chunk is empty) and for one pair: sampled windows against
+    the oracle and whole buffers against the step implementation (the
+    literal schedule)."""
+    size = -(-t // n)
+    dist = "int_uniform" if dtype == "int32" else "normal"
+    params = _params(dist, n) if dtype == "int32" else {"std": 1e-3}
+
+    def draw():
+        return [workloads.device_rank(dist, dtype, t, 47, r, DEV, params) for r in range(n)]
+
+    ar.set_impl("fused")
+    a = draw()
+    check_windows("ring_allreduce", a, lambda b: ar.ring_allreduce(b), dtype,
+                  cuts=[c * size for c in range(1, n)], seed=47, ranks=[0, n - 1])
+    ar.set_impl("step")
+    b = draw()
+    announce(f"ring_allreduce impl=step n={n} t={t} {dtype} whole buffers")
+    ar.ring_allreduce(b)
+    torch.cuda.synchronize()
+    ar.set_impl("fused")
+    view = (lambda x: x.view(torch.int16)) if dtype == "bfloat16" else (lambda x: x)
+    assert all(torch.equal(view(x), view(y)) for x, y in zip(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+
+
 def test_split_tree_allreduce_many_ranks():
     """From 12 ranks and 384 MiB of inputs the fused double-tree AllReduce runs
     as both trees' folds stored into their roots (rank 0, rank N-1), then the

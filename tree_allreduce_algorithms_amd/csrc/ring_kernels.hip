@@ -111,7 +111,11 @@ __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
 // the word's one or two elements) in slot order, and the results go to every
 // rank (ALL) or to rank c.  More than kStageGroup ranks are staged in groups
 // of equal size, each thread carrying its partials in registers.
-template <ar_dtype_t DT, ar_op_t OP, bool ALL, int NMAX>
+// The blocks take the chunks one after another (blockIdx.y is the chunk), or
+// with PAIRS two chunks at a time: block b of a one-dimensional grid is tile
+// (b mod 2T) / 2 of chunk 2 (b / 2T) + b mod 2, T = a.tiles, one tile each
+// (see fold_in_pairs).
+template <ar_dtype_t DT, ar_op_t OP, bool ALL, int NMAX, bool PAIRS>
 __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
   using T = typename Elem<DT>::T;
   constexpr int K = 16 / sizeof(T);
@@ -124,7 +128,21 @@ __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
   extern __shared__ Raw16 stage[];
 
   const int n = a.n;
-  const int c = blockIdx.y;
+  int c;
+  uint64_t tile0, tstride;
+  if constexpr (PAIRS) {
+    const uint32_t per_pair = 2u * static_cast<uint32_t>(a.tiles);
+    const uint32_t pair = blockIdx.x / per_pair;
+    const uint32_t rem = blockIdx.x - pair * per_pair;
+    c = static_cast<int>(2u * pair + (rem & 1u));
+    tile0 = rem >> 1;
+    tstride = a.tiles;
+  } else {
+    c = static_cast<int>(blockIdx.y);
+    tile0 = blockIdx.x;
+    tstride = gridDim.x;
+  }
+  if (c >= n) return;   // the second chunk of the last pair when N is odd
   const uint64_t lo = umin(static_cast<uint64_t>(c) * a.chunk, a.count);
   const uint64_t hi = umin(lo + a.chunk, a.count);
   if (lo >= hi) return;
@@ -135,7 +153,7 @@ __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
   const int groups = (n + G - 1) / G;
   const int gsize = (n + groups - 1) / groups;
 
-  for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+  for (uint64_t tile = tile0; tile < a.tiles; tile += tstride) {
     const uint64_t tp0 = (s.plo / TP + tile) * TP;
     if (tp0 >= s.phi || s.plo >= s.phi) break;
     const StageTile t{tp0, s.plo, s.phi};
@@ -172,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
       stage_out<1, M>(a.ptrs, c, c + 1, t, res);
   }
 
-  if (blockIdx.x == 0 && threadIdx.x < s.scalar_count()) {
+  if (tile0 == 0 && threadIdx.x < s.scalar_count()) {
     using FS = Fold<DT, OP, S>;
     const uint64_t e = s.scalar_index(threadIdx.x);
     typename FS::A acc = FS::widen(load<S>(a.ptrs.p[first], e));
@@ -187,14 +205,28 @@ __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
   }
 }
 
-template <ar_dtype_t DT, ar_op_t OP, bool ALL>
+template <ar_dtype_t DT, ar_op_t OP, bool ALL, bool PAIRS = false>
 const void* ring_stage_fn(int n) {
-  if (n <= 2) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 2>);
-  if (n <= 4) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 4>);
-  if (n <= 8) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 8>);
-  if (n <= 16) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 16>);
-  if (n <= 32) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 32>);
-  return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, AR_MAX_RANKS>);
+  if (n <= 2) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 2, PAIRS>);
+  if (n <= 4) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 4, PAIRS>);
+  if (n <= 8) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 8, PAIRS>);
+  if (n <= 16) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 16, PAIRS>);
+  if (n <= 32) return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, 32, PAIRS>);
+  return reinterpret_cast<const void*>(&ring_stage_kernel<DT, OP, ALL, AR_MAX_RANKS, PAIRS>);
+}
+
+// Whether the one-pass AllReduce deals its blocks over two chunks at a time.
+// Chunk after chunk, the blocks in flight read and write one narrow stretch
+// of each of the N buffers; over all N chunks at once (tiles dealt round the
+// chunks), N stretches of each.  Measured on gfx950 (in-process A/B, three
+// processes, float32 unless noted), two chunks at a time against one: N=8 x
+// 1.2 GB -0.5 to -1.1 %, N=8 x 600 MB bfloat16 -2 to -3 %, N=8 x 512 MiB -1
+// to -7 %, N=10 x 480 MB -1.4 to -2.4 %, N=16 x 600 MB -2.4 %, N=4 x 2.4 GB
+// -2 %, N=2 x 4.8 GB -2.3 %; but N=4 x 256 MiB +9 % and N=8 x 26 MB +0.4 to
+// +2.4 %, and every chunk at once N=8 x 1.2 GB +5 %, the ReduceScatter +4 to
+// +12 %.  So pairs from 384 MiB per rank, AllReduce only.
+inline bool fold_in_pairs(bool all, uint64_t count, size_t isz) {
+  return all && count * isz >= (384ull << 20);
 }
 
 template <ar_dtype_t DT, ar_op_t OP>
@@ -202,6 +234,11 @@ hipError_t ring_fold_typed(FoldArgs a, bool all, bool vec, hipStream_t stream) {
   constexpr int K = 16 / sizeof(typename Elem<DT>::T);
   if (vec && stage_ring(a.n)) {
     a.tiles = stage_tiles_for(a.chunk, K, stage_runs(a.n));
+    const uint64_t pair_blocks = static_cast<uint64_t>((a.n + 1) / 2) * 2 * a.tiles;
+    if (fold_in_pairs(all, a.count, sizeof(typename Elem<DT>::T)) && pair_blocks <= kMaxGridX) {
+      return launch(ring_stage_fn<DT, OP, true, true>(a.n), dim3(static_cast<uint32_t>(pair_blocks)), a,
+                    stream, stage_bytes(a.n));
+    }
     const dim3 grid(grid_x(a.tiles), a.n);
     const void* fn = all ? ring_stage_fn<DT, OP, true>(a.n) : ring_stage_fn<DT, OP, false>(a.n);
     return launch(fn, grid, a, stream, stage_bytes(a.n));
