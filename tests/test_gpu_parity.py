@@ -640,18 +640,20 @@ def test_split_ring_allreduce_many_ranks():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("coll", ["ring_allreduce", "tree_allreduce"])
 @pytest.mark.parametrize("n,t,dtype", [
-    (3, 100_663_296, "int32"),      # exactly 384 MiB per rank: chunks in pairs, N odd
-    (3, 100_663_295, "int32"),      # one element less: chunk after chunk
-    (11, 100_663_297, "float32"),   # pairs, N odd, ragged chunks, below the split
-    (2, 201_326_593, "bfloat16"),   # pairs, one pair
+    (3, 100_663_296, "int32"),      # exactly 384 MiB per rank: two regions at a time, N odd
+    (3, 100_663_295, "int32"),      # one element less: the plain order
+    (11, 100_663_297, "float32"),   # N odd, ragged chunks and halves, below the split
+    (2, 201_326_593, "bfloat16"),   # one pair of chunks; halves of unequal length
 ])
-def test_one_pass_allreduce_in_pairs_of_chunks(n, t, dtype):
+def test_one_pass_allreduce_two_regions_at_a_time(coll, n, t, dtype):
     """From 384 MiB per rank the one-pass ring AllReduce deals its blocks over
-    two chunks at a time.  On both sides of that size, for odd N (the last
-    pair's second chunk is empty) and for one pair: sampled windows against
-    the oracle and whole buffers against the step implementation (the
-    literal schedule)."""
+    two chunks at a time and the one-pass double tree alternates between its
+    two trees' halves.  On both sides of that size, for odd N (the ring's
+    last pair has an empty second chunk), for one pair and for halves of
+    unequal length: sampled windows against the oracle and whole buffers
+    against the step implementation (the literal schedule)."""
     size = -(-t // n)
     dist = "int_uniform" if dtype == "int32" else "normal"
     params = _params(dist, n) if dtype == "int32" else {"std": 1e-3}
@@ -659,14 +661,15 @@ def test_one_pass_allreduce_in_pairs_of_chunks(n, t, dtype):
     def draw():
         return [workloads.device_rank(dist, dtype, t, 47, r, DEV, params) for r in range(n)]
 
+    call = getattr(ar, coll)
+    cuts = [c * size for c in range(1, n)] + [-(-t // 2)]
     ar.set_impl("fused")
     a = draw()
-    check_windows("ring_allreduce", a, lambda b: ar.ring_allreduce(b), dtype,
-                  cuts=[c * size for c in range(1, n)], seed=47, ranks=[0, n - 1])
+    check_windows(coll, a, lambda b: call(b), dtype, cuts=cuts, seed=47, ranks=[0, n - 1])
     ar.set_impl("step")
     b = draw()
-    announce(f"ring_allreduce impl=step n={n} t={t} {dtype} whole buffers")
-    ar.ring_allreduce(b)
+    announce(f"{coll} impl=step n={n} t={t} {dtype} whole buffers")
+    call(b)
     torch.cuda.synchronize()
     ar.set_impl("fused")
     view = (lambda x: x.view(torch.int16)) if dtype == "bfloat16" else (lambda x: x)
