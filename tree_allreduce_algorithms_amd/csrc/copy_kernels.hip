@@ -8,7 +8,8 @@
 //
 // AllToAll: block j of rank i and block i of rank j trade places, one thread
 // per pack of the pair, so every off-diagonal element is read once and
-// written once and no two threads touch the same location.
+// written once and no two threads touch the same location.  The pairs i < j
+// are taken two at a time, their tiles dealt alternately.
 #include "device_common.hpp"
 
 namespace ar {
@@ -216,27 +217,52 @@ const void* fanout_group_fn(int u, bool ntl, bool nts) {
   return fanout_group_fn<T, 1>(ntl, nts);
 }
 
-// AllToAll block swap: blockIdx.y = i * n + j; pairs with i >= j exit (the
-// diagonal stays in place, and each pair is swapped once, by i < j).
+// AllToAll block swap over the pairs i < j (the diagonal stays in place),
+// numbered row by row: p = 0 is (0, 1), then (0, 2), ..., (0, n-1), (1, 2), ...
+// Unit u of the flattened launch is tile (u mod 2T) / 2 of pair
+// 2 (u / 2T) + u mod 2, T = a.tiles: two pairs at a time, their tiles
+// alternating; when the number of pairs is odd the last one runs alone, unit
+// u then being its tile u mod 2T.  Measured on gfx950 against one pair at a time (in-process
+// A/B): N=8 x 128 MiB -3.6 %, N=8 x 512 MiB -4.4 %, N=16 x 256 MiB -5.2 %;
+// four pairs at a time -1 to -4 %, every pair at once +5 to +8 %.
 struct AllToAllArgs {
   RankPtrs ptrs;
   uint64_t block;   // elements per block (count / n)
-  uint64_t tiles;
+  uint64_t tiles;   // tiles per pair
+  uint32_t units;   // pairs times a.tiles
   int n;
 };
+
+// The pair (i, j), i < j, numbered p in row order.
+__device__ __forceinline__ void alltoall_pair(uint32_t p, int n, int* i, int* j) {
+  int r = 0;
+  while (p >= static_cast<uint32_t>(n - 1 - r)) {
+    p -= static_cast<uint32_t>(n - 1 - r);
+    ++r;
+  }
+  *i = r;
+  *j = r + 1 + static_cast<int>(p);
+}
 
 template <class T, int U, bool VEC>
 __global__ __launch_bounds__(kBlock) void alltoall_kernel(AllToAllArgs a) {
   using P = typename PackOf<T, VEC>::P;
   constexpr int K = PackOf<T, VEC>::K;
-  const int i = static_cast<int>(blockIdx.y) / a.n;
-  const int j = static_cast<int>(blockIdx.y) % a.n;
-  if (i >= j) return;
   const uint64_t npacks = a.block / K;   // VEC only when K divides the block
   const uint64_t bbytes = a.block * sizeof(T);
-  for (uint64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+  const uint32_t pairs = static_cast<uint32_t>(a.n * (a.n - 1) / 2);
+  const uint32_t per_two = 2u * static_cast<uint32_t>(a.tiles);
+  // (the host keeps units + gridDim.x below 2^32)
+  for (uint32_t unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
+    const uint32_t two = unit / per_two;
+    const uint32_t rem = unit - two * per_two;
+    const bool alone = 2u * two + 1u >= pairs;
+    const uint32_t p = wave_uniform(static_cast<int>(alone ? 2u * two : 2u * two + (rem & 1u)));
+    int i, j;
+    alltoall_pair(p, a.n, &i, &j);
+    const uint64_t tile = alone ? rem : (rem >> 1);
     const uint64_t tp = TileGrid<U>::first_pack(0, tile);
-    if (tp >= npacks) break;
+    if (tp >= npacks) continue;
     const uint64_t toff = tp * sizeof(P);
     const TileLanes<U, sizeof(P)> ln(tp, 0, npacks);
     char* bi = at(a.ptrs.p[i], static_cast<uint64_t>(j) * bbytes + toff);   // rank i, block j
@@ -279,9 +305,14 @@ hipError_t launch_alltoall(const RankPtrs& ptrs, int n, uint64_t count, ar_dtype
   const int pack = vec ? static_cast<int>(16 / isz) : 1;
   const int u = vec ? 2 : 1;
   a.tiles = tiles_for(a.block, pack, u);
-  const dim3 grid(grid_x(a.tiles), static_cast<uint32_t>(n * n));
+  const uint64_t pairs = static_cast<uint64_t>(n) * (n - 1) / 2;
+  const uint64_t units = pairs * a.tiles;
+  // the decode runs in 32 bits: N - 1 halves of one rank's buffer in tiles
+  // of at least 1 KiB stay far below 2^32 for buffers that fit in HBM
+  if (units + kMaxGridX > UINT32_MAX) return hipErrorInvalidValue;
+  a.units = static_cast<uint32_t>(units);
   const void* fn = isz == 2 ? alltoall_fn<uint16_t>(vec) : alltoall_fn<uint32_t>(vec);
-  return launch(fn, grid, a, stream);
+  return launch(fn, dim3(grid_x(units)), a, stream);
 }
 
 namespace {
