@@ -94,7 +94,7 @@ CostCoeff g_cost[9][2] = {
     {{7.66, 6706.0}, {7.66, 6706.0}},   // Reduce (fused either way)
     {{3.32, 4224.0}, {3.32, 4224.0}},   // Scatter (one step either way)
     {{3.32, 5556.0}, {3.32, 5556.0}},   // Gather (one step either way)
-    {{3.32, 5882.0}, {3.32, 5882.0}},   // AllToAll (one kernel either way)
+    {{3.32, 6060.0}, {3.32, 6060.0}},   // AllToAll (one kernel either way)
 };
 
 bool coll_ok(int coll) { return coll >= AR_RING_ALLREDUCE && coll <= AR_ALLTOALL; }
