@@ -113,8 +113,9 @@ __global__ __launch_bounds__(kBlock) void ring_fold_kernel(FoldArgs a) {
 // of equal size, each thread carrying its partials in registers.
 // The blocks take the chunks one after another (blockIdx.y is the chunk), or
 // with PAIRS two chunks at a time: block b of a one-dimensional grid is tile
-// (b mod 2T) / 2 of chunk 2 (b / 2T) + b mod 2, T = a.tiles, one tile each
-// (see fold_in_pairs).
+// (b mod 2T) / 2 of chunk 2 (b / 2T) + b mod 2, T = a.tiles, one tile each;
+// with N odd the last chunk runs alone, block b being its tile b mod 2T (see
+// fold_in_pairs).
 template <ar_dtype_t DT, ar_op_t OP, bool ALL, int NMAX, bool PAIRS>
 __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
   using T = typename Elem<DT>::T;
@@ -134,15 +135,15 @@ __global__ __launch_bounds__(kBlock) void ring_stage_kernel(FoldArgs a) {
     const uint32_t per_pair = 2u * static_cast<uint32_t>(a.tiles);
     const uint32_t pair = blockIdx.x / per_pair;
     const uint32_t rem = blockIdx.x - pair * per_pair;
-    c = static_cast<int>(2u * pair + (rem & 1u));
-    tile0 = rem >> 1;
+    const bool alone = 2u * pair + 1u >= static_cast<uint32_t>(n);
+    c = static_cast<int>(alone ? 2u * pair : 2u * pair + (rem & 1u));
+    tile0 = alone ? rem : rem >> 1;
     tstride = a.tiles;
   } else {
     c = static_cast<int>(blockIdx.y);
     tile0 = blockIdx.x;
     tstride = gridDim.x;
   }
-  if (c >= n) return;   // the second chunk of the last pair when N is odd
   const uint64_t lo = umin(static_cast<uint64_t>(c) * a.chunk, a.count);
   const uint64_t hi = umin(lo + a.chunk, a.count);
   if (lo >= hi) return;
@@ -234,7 +235,7 @@ hipError_t ring_fold_typed(FoldArgs a, bool all, bool vec, hipStream_t stream) {
   constexpr int K = 16 / sizeof(typename Elem<DT>::T);
   if (vec && stage_ring(a.n)) {
     a.tiles = stage_tiles_for(a.chunk, K, stage_runs(a.n));
-    const uint64_t pair_blocks = static_cast<uint64_t>((a.n + 1) / 2) * 2 * a.tiles;
+    const uint64_t pair_blocks = static_cast<uint64_t>(a.n) * a.tiles;
     if (fold_in_pairs(all, a.count, sizeof(typename Elem<DT>::T)) && pair_blocks <= kMaxGridX) {
       return launch(ring_stage_fn<DT, OP, true, true>(a.n), dim3(static_cast<uint32_t>(pair_blocks)), a,
                     stream, stage_bytes(a.n));
