@@ -935,10 +935,12 @@ def test_allreduce_runs_the_chosen_algorithm(impl):
 
 def test_alltoall_block_sizes_and_involution():
     """AllToAll on block sizes that are and are not a multiple of 16 bytes
-    (16-byte packs vs one element at a time), bfloat16 and int32, N up to 64;
-    applying it twice restores the inputs."""
+    (16-byte packs vs one element at a time), bfloat16 and int32, N up to 64,
+    even and odd numbers of rank pairs (the last of an odd number runs alone,
+    over one tile or many); applying it twice restores the inputs."""
     for n, b, dtype in ((4, 1, "int32"), (8, 4096, "float32"), (8, 4097, "float32"),
-                        (64, 520, "bfloat16"), (3, 1000, "bfloat16"), (16, 33, "int32")):
+                        (64, 520, "bfloat16"), (3, 1000, "bfloat16"), (16, 33, "int32"),
+                        (2, 100_000, "float32"), (7, 40_000, "int32"), (7, 40_001, "bfloat16")):
         dist = "int_uniform" if dtype == "int32" else "normal"
         x = workloads.host_inputs(n, n * b, dtype, dist, 91 + n, _params(dist, n))
         compare_collective("alltoall", x, dtype, "sum", 0)
