@@ -597,6 +597,8 @@ SUITE = [
     ("zero_n64", "ring_allreduce", "fused", ["--flush-mall", "--warmup", "20"]),
     ("zero_n64", "tree_allreduce", "fused", ["--flush-mall", "--warmup", "20"]),
     ("large_grad_fp32", "reduce", "fused", ["--warmup", "15"]),
+    ("large_grad_fp32", "allgather", "fused", ["--warmup", "15"]),
+    ("large_grad_fp32", "broadcast", "fused", ["--warmup", "15"]),
     ("moe_alltoall", "alltoall", "fused", ["--warmup", "80"]),
     ("moe_alltoall", "alltoall", "fused", ["--flush-mall", "--warmup", "80"]),
     ("small_int32", "ring_allreduce", "fused", ["--steps", "30", "--warmup", "30"]),
