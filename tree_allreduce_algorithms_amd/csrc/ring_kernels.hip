@@ -223,9 +223,10 @@ const void* ring_stage_fn(int n) {
 // processes, float32 unless noted), two chunks at a time against one: N=8 x
 // 1.2 GB -0.5 to -1.1 %, N=8 x 600 MB bfloat16 -2 to -3 %, N=8 x 512 MiB -1
 // to -7 %, N=10 x 480 MB -1.4 to -2.4 %, N=16 x 600 MB -2.4 %, N=4 x 2.4 GB
-// -2 %, N=2 x 4.8 GB -2.3 %; but N=4 x 256 MiB +9 % and N=8 x 26 MB +0.4 to
-// +2.4 %, and every chunk at once N=8 x 1.2 GB +5 %, the ReduceScatter +4 to
-// +12 %.  So pairs from 384 MiB per rank, AllReduce only.
+// -2 %, N=2 x 4.8 GB -2.3 %; but N=4 x 256 MiB +9 %, N=6-8 at 64-256 MiB +2
+// to +5 %, N=8 x 26 MB +0.4 to +2.4 %, and every chunk at once N=8 x 1.2 GB
+// +5 %, the ReduceScatter +4 to +12 %.  So pairs from 384 MiB per rank,
+// AllReduce only.
 inline bool fold_in_pairs(bool all, uint64_t count, size_t isz) {
   return all && count * isz >= (384ull << 20);
 }
