@@ -193,3 +193,22 @@ def test_kernel_hash_follows_includes(tmp_path):
     assert bench.kernel_source_hash(None, csrc=str(tmp_path)) == h0
     (tmp_path / "deep.hpp").write_text("int d2;\n")
     assert bench.kernel_source_hash(None, csrc=str(tmp_path)) != h0
+
+
+def test_committed_profiles_match_the_current_kernels():
+    """Every profile summary records the hash of the device code it was taken
+    on; each must match the current sources (its kernel's, or all of them for
+    a summary over several kernels), so no committed figure describes code
+    that has since changed."""
+    keys = [None] + sorted(bench.KERNEL_FILE)
+    current = {k: bench.kernel_source_hash(k) for k in keys}
+    stale = []
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        text = open(path).read()
+        found = re.findall(r"kernel_source_sha256(?: \((\w+)\))?:\s*([0-9a-f]{64})", text)
+        assert found, f"{os.path.basename(path)} records no source hash"
+        for key, sha in found:
+            ok = sha == current.get(key) if key else sha in current.values()
+            if not ok:
+                stale.append((os.path.basename(path), key))
+    assert not stale, stale
